@@ -1,0 +1,132 @@
+"""Oracle of the setup step: per-sequence metadata and tile work lists.
+
+TEST INFRASTRUCTURE (see ``oracle/attention.py``).  This is an independent
+restatement of what the on-device setup step must produce, compared with it bit
+for bit.  The pages ask for the per-sequence base rows to come from the bound
+offsets on device, with no device-to-host read (cudnn-frontend issue on padded
+THD, "Proposal": the setup step already writes device metadata and could read
+the caller's ragged offsets; validating device prefix sums on the host would
+need the read a previous change removed), with one base per tensor (the
+metadata must widen beyond one cu_q/cu_k pair).  The list format and its order
+are this library's own design:
+
+* Per sequence b: ``lq, lk, policy, diag, flags`` (int32) and one int64 base
+  per tensor in the order Q, K, V, O, LSE, dO, dQ, dK, dV (backward-only bases
+  are 0 in a forward setup).  ``flags`` = 1 if the sequence is valid, plus its
+  status bits shifted left by 8.
+* Forward tile list (one int32 pair (b, t) per tile of ``bm`` query rows):
+  valid sequences with ``lq > 0``, ordered by descending cost then ascending b,
+  each sequence's tiles from last to first.  The cost of a sequence is the sum
+  over its tiles of ``max(1, ceil(kv_end / bn))``, ``kv_end`` being the key
+  bound of the tile's last row (``lk`` for padding; ``clamp(row_end + diag, 0,
+  lk)`` for causal).
+* Backward kv-tile list (int32 quadruple (b_first, n_members, u, lk_max) per
+  tile of ``bn_b`` key rows of a kv group): a kv group is a maximal run of
+  consecutive valid sequences with ``lk > 0`` whose K, V, dK and dV bases are
+  all equal (segments binding the same K/V rows, e.g. context-parallel query
+  chunks of one document).  Groups are ordered by descending cost (sum of the
+  members' costs under the backward tile sizes) then ascending b_first; tiles
+  of a group in ascending u over ``ceil(lk_max / bn_b)``.
+* If a list would exceed its capacity (more tiles than the output buffer's rows
+  can hold, which only happens when sequences overlap), the overflow bit is set
+  and both tile counts are 0: nothing is computed.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, ST_LIST_OVERFLOW,
+                        Problem, Tensor, sequence_info)
+
+BASE_ORDER = ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def rows_capacity(t: Tensor) -> int:
+    """Largest row count r such that row r-1 (all heads, all dims) still fits."""
+    extra = (t.heads - 1) * t.stride_h + (t.dim - 1)
+    return (t.span - 1 - extra) // t.stride_t + 1
+
+
+def tile_cost(lq: int, lk: int, causal: bool, diag: int, bm: int, bn: int) -> int:
+    cost = 0
+    for t in range(ceil_div(lq, bm)):
+        row_end = min(lq, (t + 1) * bm)
+        kv_end = lk if not causal else min(max(row_end + diag, 0), lk)
+        cost += max(1, ceil_div(kv_end, bn))
+    return cost
+
+
+def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
+          bm_b: int = 0, bn_b: int = 0, cap_fwd: int, cap_bwd: int = 0) -> dict:
+    """Expected setup outputs.  ``tensors`` maps q k v o lse (+ do dq dk dv)
+    to oracle Tensors."""
+    if backward:
+        q_side = [tensors[n] for n in ("q", "o", "lse", "do", "dq")]
+        kv_side = [tensors[n] for n in ("k", "v", "dk", "dv")]
+    else:
+        q_side = [tensors[n] for n in ("q", "o", "lse")]
+        kv_side = [tensors[n] for n in ("k", "v")]
+    B = prob.batch
+    lq = np.zeros(B, np.int32)
+    lk = np.zeros(B, np.int32)
+    pol = np.zeros(B, np.int32)
+    diag = np.zeros(B, np.int32)
+    flags = np.zeros(B, np.int32)
+    base = np.zeros((9, B), np.int64)
+    status = 0
+    infos = []
+    for b in range(B):
+        info = sequence_info(prob, q_side, kv_side, b)
+        infos.append(info)
+        lq[b], lk[b], pol[b], diag[b] = info.lq, info.lk, info.policy, info.diag
+        flags[b] = (1 if info.valid else 0) | (info.status << 8)
+        status |= info.status
+        for i, n in enumerate(BASE_ORDER):
+            if n in tensors and (backward or i < 5):
+                base[i, b] = int(tensors[n].ragged[b])
+
+    def cost_of(b, tm, tn):
+        i = infos[b]
+        return tile_cost(i.lq, i.lk, i.policy in (CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT),
+                         i.diag, tm, tn)
+
+    listed = [b for b in range(B) if infos[b].valid and infos[b].lq > 0]
+    order = sorted(listed, key=lambda b: (-cost_of(b, bm, bn), b))
+    fwd = []
+    for b in order:
+        for t in range(ceil_div(infos[b].lq, bm) - 1, -1, -1):
+            fwd.append((b, t))
+
+    bwd = []
+    if backward:
+        groups = []  # (first, n)
+        b = 0
+        while b < B:
+            if not (infos[b].valid and infos[b].lk > 0):
+                b += 1
+                continue
+            first = b
+            while (b + 1 < B and infos[b + 1].valid and infos[b + 1].lk > 0
+                   and all(base[i, b + 1] == base[i, first] for i in (1, 2, 7, 8))):
+                b += 1
+            groups.append((first, b - first + 1))
+            b += 1
+        gcost = [sum(cost_of(m, bm_b, bn_b) for m in range(f, f + n)) for f, n in groups]
+        gorder = sorted(range(len(groups)), key=lambda g: (-gcost[g], groups[g][0]))
+        for g in gorder:
+            f, n = groups[g]
+            lmax = max(infos[m].lk for m in range(f, f + n))
+            for u in range(ceil_div(lmax, bn_b)):
+                bwd.append((f, n, u, lmax))
+
+    if len(fwd) > cap_fwd or (backward and len(bwd) > cap_bwd):
+        status |= ST_LIST_OVERFLOW
+        fwd, bwd = [], []
+    return dict(lq=lq, lk=lk, policy=pol, diag=diag, flags=flags, base=base,
+                fwd=np.asarray(fwd, np.int32).reshape(-1, 2),
+                bwd=np.asarray(bwd, np.int32).reshape(-1, 4),
+                status=status, infos=infos)

@@ -1,0 +1,82 @@
+"""Pins of the setup-step oracle (oracle/worklist.py) against hand-computed lists."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle import worklist
+
+
+def _problem(lq, lk, policy, qco=None):
+    B = len(lq)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    return oracle.Problem(1, 1, 8, 1.0, cu_q, cu_k, np.asarray(policy, np.int8), 0,
+                          None if qco is None else np.asarray(qco, np.int32))
+
+
+def _tensors(q_start, kv_start, q_rows, kv_rows, lse_rows=None, heads=1, dim=8):
+    def t(rows, start, d=dim, st=None):
+        st = heads * d if st is None else st
+        return oracle.Tensor(np.zeros(rows * st, np.uint16 if d > 1 else np.float32), st, d,
+                             np.asarray(start, np.int64) * st, heads, d)
+    out = {n: t(q_rows, q_start) for n in ("q", "o", "do", "dq")}
+    out.update({n: t(kv_rows, kv_start) for n in ("k", "v", "dk", "dv")})
+    out["lse"] = t(q_rows if lse_rows is None else lse_rows, q_start, d=1)
+    return out
+
+
+def test_forward_and_backward_lists_by_hand():
+    # lq [5,0,3,9], lk [5,2,7,4], policies [top-left, padding, bottom-right, padding]
+    # bm = 4, bn = 2.  Costs (sum over q tiles of max(1, ceil(kv_end/2))):
+    #   b0: tiles rows 0-3 -> kv_end 4 -> 2; row 4 -> kv_end 5 -> 3      => 5
+    #   b1: no query rows                                                => 0 (not listed)
+    #   b2: diag = 7-3 = 4; rows 0-2 -> kv_end min(3+4, 7) = 7 -> 4       => 4
+    #   b3: padding, 3 tiles x ceil(4/2)=2                                => 6
+    prob = _problem([5, 0, 3, 9], [5, 2, 7, 4], [1, 0, 2, 0])
+    t = _tensors([0, 5, 5, 8, 17], [0, 5, 7, 14, 18], 17, 18)
+    s = worklist.setup(prob, t, backward=True, bm=4, bn=2, bm_b=4, bn_b=2, cap_fwd=100,
+                       cap_bwd=100)
+    assert s["status"] == 0
+    assert s["fwd"].tolist() == [[3, 2], [3, 1], [3, 0], [0, 1], [0, 0], [2, 0]]
+    # kv groups: one per valid sequence with lk > 0 (bases all differ), ordered by
+    # the same costs under (bm_b, bn_b) = (4, 2): b3 6, b0 5, b2 4, b1 0.
+    assert s["bwd"].tolist() == [[3, 1, 0, 4], [3, 1, 1, 4],
+                                 [0, 1, 0, 5], [0, 1, 1, 5], [0, 1, 2, 5],
+                                 [2, 1, 0, 7], [2, 1, 1, 7], [2, 1, 2, 7], [2, 1, 3, 7],
+                                 [1, 1, 0, 2]]
+    assert s["diag"].tolist() == [0, 0, 4, 0]
+    assert s["flags"].tolist() == [1, 1, 1, 1]
+    assert s["base"][0].tolist() == [0, 40, 40, 64]          # Q rows 0, 5, 5, 8 (x 8)
+    assert s["base"][4].tolist() == [0, 5, 5, 8]             # LSE token stride 1
+
+
+def test_aliasing_segments_form_one_kv_group():
+    # four query chunks; chunks 0,1 bind K/V rows of document 0, chunks 2,3 of doc 1
+    prob = _problem([4, 4, 4, 4], [16, 16, 16, 16], [1, 1, 1, 1], qco=[4, 12, 4, 12])
+    t = _tensors([0, 4, 8, 12, 16], [0, 0, 16, 16, 32], 16, 32)
+    s = worklist.setup(prob, t, backward=True, bm=4, bn=8, bm_b=4, bn_b=8, cap_fwd=100,
+                       cap_bwd=100)
+    # costs: chunk at offset 4: kv_end = 4+4 = 8 -> 1 tile; offset 12: 16 -> 2 tiles.
+    assert s["fwd"].tolist() == [[1, 0], [3, 0], [0, 0], [2, 0]]
+    # two groups of 2 members, cost 3 each -> ascending b_first; 2 kv tiles each
+    assert s["bwd"].tolist() == [[0, 2, 0, 16], [0, 2, 1, 16], [2, 2, 0, 16], [2, 2, 1, 16]]
+
+
+def test_invalid_and_overflow():
+    prob = _problem([4, 4], [4, 4], [0, 7])
+    t = _tensors([0, 4, 8], [0, 4, 8], 8, 8)
+    s = worklist.setup(prob, t, backward=False, bm=2, bn=2, cap_fwd=100)
+    assert s["status"] == oracle.ST_BAD_POLICY
+    assert s["flags"].tolist() == [1, oracle.ST_BAD_POLICY << 8]
+    assert s["fwd"].tolist() == [[0, 1], [0, 0]]
+    s = worklist.setup(prob, t, backward=False, bm=2, bn=2, cap_fwd=1)
+    assert s["status"] == oracle.ST_BAD_POLICY | oracle.ST_LIST_OVERFLOW
+    assert s["fwd"].shape == (0, 2)
+
+
+def test_rows_capacity():
+    t = oracle.Tensor(np.zeros(13 * 2 * 64, np.uint16), 128, 64, np.zeros(4, np.int64), 2, 64)
+    assert worklist.rows_capacity(t) == 13
+    hm = oracle.Tensor(np.zeros(8 * 7360, np.float32), 1, 7360, np.zeros(2, np.int64), 8, 1)
+    assert worklist.rows_capacity(hm) == 7360
