@@ -1,0 +1,252 @@
+/*
+ * varlen_attn.h -- C ABI of the MI355X (gfx950) ragged THD attention library.
+ *
+ * Scaled-dot-product attention over ragged, THD-packed batches: a forward pass
+ * that also emits the softmax statistics (log-sum-exp, LSE), and a backward
+ * pass producing dQ, dK and dV.  Every entry point only validates host-visible
+ * arguments and enqueues HIP kernels on the caller's stream; it allocates
+ * nothing, keeps no state between calls, copies nothing between host and
+ * device and never synchronises, so it can be captured in a HIP graph.
+ *
+ * Addressing (cudnn-frontend issue on padded THD, sections "Concrete failure"
+ * and "Proposal: consume the bound offsets on device"): row i of sequence b of
+ * tensor X, head h, element d lives at
+ *
+ *     X.data[X.ragged[b] + i * X.stride_t + h * X.stride_h + d]
+ *
+ * with X.ragged a caller-bound device array of element offsets, one array per
+ * tensor, so Q/O padding may differ from K/V padding.  Offsets are never
+ * re-derived from the sequence lengths.  Lengths come from the cumulative
+ * valid-length arrays: Lq(b) = cu_seqlens_q[b+1] - cu_seqlens_q[b], likewise
+ * Lk(b) from cu_seqlens_kv; they bound the mask and decide dead rows.
+ *
+ * Mask (per sequence; TransformerEngine PR #3274, "Description" and the
+ * reviewer's policy mapping; Megatron-LM PR #14 commit message for the
+ * diagonals): key j is visible to row i iff j < Lk(b) and either the policy is
+ * VARLEN_ATTN_PADDING or j <= i + delta(b), where delta(b) is
+ *   0                    for VARLEN_ATTN_CAUSAL_TOP_LEFT,
+ *   Lk(b) - Lq(b)        for VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT,
+ *   q_causal_offset[b]   for either causal policy when that array is given
+ *                        (the absolute key index of the segment's q[0]).
+ * A row with no visible key is dead: O = 0, LSE = -inf, dQ = 0.
+ *
+ * LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32, in
+ * any strided layout: token-major [t, h] (stride_t = H_q, stride_h = 1) or
+ * head-major [h, t] (stride_t = 1, stride_h >= rows), each with its own ragged
+ * offsets in its own element units (cudnn-frontend PR #462, "What").
+ *
+ * Buffers the kernels never write: pad rows between or around sequences,
+ * gap columns of strided views, rows of invalid sequences.  Those elements of
+ * O, LSE, dQ, dK and dV keep their previous contents bit for bit.
+ *
+ * Data types: Q, K, V, O, dO, dQ, dK, dV are bf16 (stored as uint16 bit
+ * patterns, round-to-nearest-even on output); LSE and the scale are fp32.
+ */
+#ifndef VARLEN_ATTN_H
+#define VARLEN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- codes */
+
+/* Host return codes.  A nonzero code means nothing was enqueued. */
+enum {
+  VARLEN_ATTN_OK = 0,
+  VARLEN_ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  VARLEN_ATTN_ERR_BATCH = 2,       /* batch < 0 */
+  VARLEN_ATTN_ERR_HEAD_DIM = 3,    /* head_dim not 64 or 128 */
+  VARLEN_ATTN_ERR_HEADS = 4,       /* h_q or h_kv < 1, or h_q % h_kv != 0 */
+  VARLEN_ATTN_ERR_ALIGN = 5,       /* bf16 data not 16-byte aligned, LSE not
+                                      4-byte aligned, workspace not 256-byte
+                                      aligned */
+  VARLEN_ATTN_ERR_STRIDE = 6,      /* bf16 strides not multiples of 8, or a
+                                      stride smaller than one row/head, or
+                                      larger than the span */
+  VARLEN_ATTN_ERR_SPAN = 7,        /* span_elems smaller than one row */
+  VARLEN_ATTN_ERR_WORKSPACE = 8,   /* workspace NULL or too small */
+  VARLEN_ATTN_ERR_POLICY = 9,      /* default_policy not 0, 1 or 2 */
+  VARLEN_ATTN_ERR_SCALE = 10,      /* scale not finite */
+  VARLEN_ATTN_ERR_HIP = 11         /* a HIP launch failed */
+};
+
+/* Mask policies (TransformerEngine names: padding, padding_causal,
+ * padding_causal_bottom_right). */
+enum {
+  VARLEN_ATTN_PADDING = 0,
+  VARLEN_ATTN_CAUSAL_TOP_LEFT = 1,
+  VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT = 2
+};
+
+/* Device status bits.  Device-resident arguments (lengths, offsets,
+ * policies) cannot be checked on the host without the device-to-host read
+ * the pages rule out (cudnn-frontend issue on padded THD, "Proposal").  The
+ * setup kernel checks them instead: an offending sequence is skipped (its
+ * outputs stay untouched) and its bits are ORed into *dev_status. */
+enum {
+  VARLEN_ATTN_ST_NEG_LENGTH = 1,     /* Lq < 0 or Lk < 0 */
+  VARLEN_ATTN_ST_BAD_OFFSET = 2,     /* ragged[b] < 0, or a bf16 tensor's
+                                        ragged[b] not a multiple of 8 */
+  VARLEN_ATTN_ST_OUT_OF_SPAN = 4,    /* a row of the sequence would reach past
+                                        span_elems */
+  VARLEN_ATTN_ST_BAD_POLICY = 8,     /* mask_policy[b] not 0, 1 or 2 */
+  VARLEN_ATTN_ST_LIST_OVERFLOW = 16  /* more tiles than the output buffers'
+                                        rows can hold (sequences overlap):
+                                        nothing is computed */
+};
+
+/* ---------------------------------------------------------------- types */
+
+/* One ragged tensor as the caller binds it.  All pointers are device
+ * pointers owned by the caller.  Element strides; the innermost (head_dim)
+ * stride is 1.  `span_elems` is the number of elements addressable from
+ * `data` (the allocation's or view's element span, not the count of valid
+ * tokens: cudnn-frontend PR #462, review of the sizing helper and "Not
+ * addressed here").  `ragged` holds batch + 1 int64 element offsets; entry
+ * `batch` (past-the-end) is not used for addressing. */
+typedef struct varlen_attn_tensor {
+  void* data;
+  int64_t span_elems;
+  int64_t stride_t;
+  int64_t stride_h;
+  const int64_t* ragged;
+} varlen_attn_tensor;
+
+/* The problem.  cu_seqlens_q/kv: device int32 [batch+1] cumulative valid
+ * lengths.  mask_policy: device int8 [batch] or NULL (then default_policy
+ * applies to every sequence).  q_causal_offset: device int32 [batch] or NULL
+ * (then each causal policy uses its own alignment).  GQA: query head h reads
+ * key/value head h / (h_q / h_kv). */
+typedef struct varlen_attn_problem {
+  int32_t batch;
+  int32_t h_q;
+  int32_t h_kv;
+  int32_t head_dim;
+  float scale;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_kv;
+  const int8_t* mask_policy;
+  int32_t default_policy;
+  const int32_t* q_causal_offset;
+} varlen_attn_problem;
+
+/* Byte offsets of the workspace regions (each 256-byte aligned) and the tile
+ * sizes the kernels use.  Regions are separate so that no buffer can run into
+ * another's counters (cudnn-frontend PR #462, "Root cause": an overrun of one
+ * intermediate clobbered the next region's tile counter).
+ *   counters  int32[64]  tile-claim counters, zeroed by the setup kernel
+ *   header    int32[16]  [0] forward tiles, [1] backward tiles, [2] status
+ *   seq       int32 lq[B], lk[B], policy[B], diag[B], flags[B] (flags: bit 0
+ *             valid, status bits << 8), then at seq + seq_i64_offset int64
+ *             base[9][B] in the order Q, K, V, O, LSE, dO, dQ, dK, dV
+ *   fwd_tiles int32[2 * capacity]: (b, t) for the t-th tile of fwd_block_m
+ *             query rows of sequence b
+ *   bwd_tiles int32[4 * capacity]: (first b, members, u, max Lk) for the u-th
+ *             tile of bwd_block_n key rows of a group of consecutive
+ *             sequences that bind the same K, V, dK and dV rows
+ *   scratch   setup kernel scratch
+ *   delta     fp32, same element offsets as LSE (backward only)
+ *   dq_accum  fp32, same element offsets as dQ (backward only) */
+typedef struct varlen_attn_layout {
+  int64_t total_bytes;
+  int64_t counters_offset;
+  int64_t header_offset;
+  int64_t seq_offset;
+  int64_t seq_i64_offset;
+  int64_t fwd_tiles_offset;
+  int64_t fwd_tiles_capacity;
+  int64_t bwd_tiles_offset;
+  int64_t bwd_tiles_capacity;
+  int64_t scratch_offset;
+  int64_t delta_offset;
+  int64_t delta_elems;
+  int64_t dq_accum_offset;
+  int64_t dq_accum_elems;
+  int32_t fwd_block_m;
+  int32_t fwd_block_n;
+  int32_t bwd_block_m;
+  int32_t bwd_block_n;
+} varlen_attn_layout;
+
+/* ---------------------------------------------------------------- sizing */
+
+/* Workspace layout of a forward call.  Host only (reads no device memory).
+ * The tile capacity comes from o's physical row capacity,
+ * floor((span - 1 - (h_q-1)*stride_h - (D-1)) / stride_t) + 1, plus batch:
+ * never from the number of valid tokens. */
+int varlen_attn_fwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* o,
+                                     varlen_attn_layout* out);
+
+/* Workspace layout of a backward call.  delta mirrors lse and dq_accum
+ * mirrors dq element for element, so they are sized from the caller's spans
+ * of those tensors, which count every axis (cudnn-frontend PR #462, "The fix
+ * (commit 1)": size from every stride axis; a head-major [h, t] LSE needs
+ * h*t elements, not t).  Host only. */
+int varlen_attn_bwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
+                                     const varlen_attn_tensor* dq, const varlen_attn_tensor* dk,
+                                     varlen_attn_layout* out);
+
+/* total_bytes of the layouts above. */
+int varlen_attn_fwd_workspace_size(const varlen_attn_problem* p, const varlen_attn_tensor* o,
+                                   size_t* bytes);
+int varlen_attn_bwd_workspace_size(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
+                                   const varlen_attn_tensor* dq, const varlen_attn_tensor* dk,
+                                   size_t* bytes);
+
+/* ---------------------------------------------------------------- compute */
+
+/* Forward.  Reads q, k, v (bf16); writes o (bf16) and lse (fp32) for the
+ * valid rows of valid sequences only.  `workspace` (device, 256-byte aligned,
+ * at least varlen_attn_fwd_workspace_size bytes) is overwritten.
+ * `dev_status` (device int32, may be NULL) receives device status bits by
+ * atomic OR; the caller clears it.  `stream` is a hipStream_t (NULL: the
+ * default stream).  batch == 0 returns VARLEN_ATTN_OK with nothing enqueued.
+ * Returns a host code; on nonzero nothing was enqueued. */
+int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                    const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                    const varlen_attn_tensor* o, const varlen_attn_tensor* lse, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/* Backward.  Reads q, k, v, o, dout (bf16) and lse (fp32, as written by the
+ * forward); writes dq, dk, dv (bf16) for valid rows only.  dK and dV of key
+ * rows bound by several consecutive sequences (identical K, V, dK and dV
+ * offsets, e.g. context-parallel query chunks of one document) are the sums
+ * over those sequences.  Other overlaps between the output rows of different
+ * sequences are not allowed and not checked.  Workspace, status and stream as
+ * for the forward. */
+int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                    const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                    const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                    const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                    const varlen_attn_tensor* dk, const varlen_attn_tensor* dv, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/* The setup kernel alone, as the forward (varlen_attn_fwd_setup) or the
+ * backward (varlen_attn_bwd_setup) runs it first: per-sequence metadata,
+ * validity and tile lists in the workspace regions described by
+ * varlen_attn_layout.  Same arguments and codes as the full calls. */
+int varlen_attn_fwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                          const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                          const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                          void* stream);
+int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                          const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                          const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                          const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                          const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                          void* stream);
+
+/* Static text for a host return code. */
+const char* varlen_attn_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARLEN_ATTN_H */

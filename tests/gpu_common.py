@@ -1,0 +1,89 @@
+"""Comparison helpers for the GPU tests (HIP path vs the fp64 oracle)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import workloads
+from tests._util import bf16_to_f64
+
+# Tolerances (max-abs vs fp64) for the HIP path.
+O_TOL = 2e-2
+GRAD_TOL = 5e-2
+LSE_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def pre_fill(batch: workloads.Batch, n: str) -> np.ndarray:
+    lay = batch.layouts[n]
+    return workloads.out_buffer(lay, "f32" if n == "lse" else "bf16")
+
+
+def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what=""):
+    """Written elements within `tol` of the oracle; all others bit-identical
+    to the pre-call contents."""
+    pre = pre_fill(batch, n)
+    assert gpu_bits.shape == pre.shape
+    untouched = ~written
+    bad = np.nonzero(gpu_bits[untouched] != pre[untouched])[0]
+    assert bad.size == 0, f"{what}{n}: {bad.size} elements outside valid rows were written"
+    if written.any():
+        g = bf16_to_f64(gpu_bits[written])
+        r = ref_vals[written]
+        assert np.all(np.isfinite(g)), f"{what}{n}: non-finite output in a valid row"
+        err = np.abs(g - r)
+        assert err.max() <= tol, (f"{what}{n}: max abs err {err.max():.3e} > {tol} "
+                                  f"(at {np.argmax(err)}, gpu {g[np.argmax(err)]}, "
+                                  f"ref {r[np.argmax(err)]})")
+        return float(err.max())
+    return 0.0
+
+
+def compare_lse(batch, gpu, ref, written, what=""):
+    pre = pre_fill(batch, "lse")
+    untouched = ~written
+    assert np.array_equal(gpu[untouched].view(np.uint32), pre[untouched].view(np.uint32)), \
+        f"{what}lse: elements outside valid rows were written"
+    if not written.any():
+        return 0.0
+    g, r = gpu[written].astype(np.float64), ref[written]
+    dead = r == -np.inf
+    assert np.all(g[dead] == -np.inf), f"{what}lse: dead rows must be -inf"
+    assert np.all(np.isfinite(g[~dead])), f"{what}lse: non-finite LSE on a live row"
+    err = np.abs(g[~dead] - r[~dead])
+    m = float(err.max()) if err.size else 0.0
+    assert m <= LSE_TOL, f"{what}lse: max abs err {m:.3e}"
+    return m
+
+
+def oracle_fwd(batch):
+    prob, t = oracle.from_batch(batch)
+    return oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"])
+
+
+def oracle_bwd(batch, kv_heads=None):
+    prob, t = oracle.from_batch(batch)
+    return oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                           t["dk"], t["dv"], kv_heads=kv_heads)
+
+
+def check_forward(batch, dev, ref=None, what=""):
+    ref = oracle_fwd(batch) if ref is None else ref
+    eo = compare_bf16(batch, "o", dev.host("o"), ref["o"], ref["o_written"], O_TOL, what)
+    el = compare_lse(batch, dev.host("lse"), ref["lse"], ref["lse_written"], what)
+    assert int(dev.status.item()) == ref["status"], (dev.status.item(), ref["status"])
+    return eo, el
+
+
+def check_backward(batch, dev, ref=None, what=""):
+    ref = oracle_bwd(batch) if ref is None else ref
+    errs = {}
+    for n in ("dq", "dk", "dv"):
+        errs[n] = compare_bf16(batch, n, dev.host(n), ref[n], ref[n + "_written"], GRAD_TOL, what)
+    return errs

@@ -1,0 +1,327 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import worklist
+from tests.gpu_common import (GRAD_TOL, O_TOL, check_backward, check_forward, compare_bf16,
+                              oracle_bwd, oracle_fwd, pre_fill, say)
+from tests._util import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import variable_length_attention_ragged_amd as va
+    va.lib()  # fail loudly if the library is missing
+
+
+def _dev(batch, with_grad=None):
+    from workloads.device import DeviceBatch
+    return DeviceBatch(batch, with_grad=with_grad)
+
+
+# ------------------------------------------------------------------ setup kernel
+
+def _read_setup(ws, L, B):
+    raw = ws.cpu().numpy().view(np.uint8)
+    i32 = lambda off, n: raw[off:off + 4 * n].view(np.int32)
+    header = i32(L.header_offset, 16)
+    seq = i32(L.seq_offset, 5 * B).reshape(5, B)
+    base = raw[L.seq_offset + L.seq_i64_offset:L.seq_offset + L.seq_i64_offset + 72 * B] \
+        .view(np.int64).reshape(9, B)
+    fwd = i32(L.fwd_tiles_offset, 2 * int(header[0])).reshape(-1, 2)
+    bwd = i32(L.bwd_tiles_offset, 4 * int(header[1])).reshape(-1, 4) if header[1] > 0 else \
+        np.zeros((0, 4), np.int32)
+    counters = i32(L.counters_offset, 64)
+    return header, seq, base, fwd, bwd, counters
+
+
+def _check_setup(batch, backward):
+    dev = _dev(batch, with_grad=backward)
+    L = dev.bwd_layout() if backward else dev.fwd_layout()
+    ws = torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda")
+    (dev.bwd_setup if backward else dev.fwd_setup)(workspace=ws)
+    torch.cuda.synchronize()
+    header, seq, base, fwd, bwd, counters = _read_setup(ws, L, batch.batch)
+    prob, t = oracle.from_batch(batch)
+    if not backward:
+        t = {n: t[n] for n in ("q", "k", "v", "o", "lse")}
+    exp = worklist.setup(prob, t, backward=backward, bm=L.fwd_block_m, bn=L.fwd_block_n,
+                         bm_b=L.bwd_block_m, bn_b=L.bwd_block_n,
+                         cap_fwd=L.fwd_tiles_capacity, cap_bwd=L.bwd_tiles_capacity)
+    np.testing.assert_array_equal(seq[0], exp["lq"])
+    np.testing.assert_array_equal(seq[1], exp["lk"])
+    np.testing.assert_array_equal(seq[2], exp["policy"])
+    np.testing.assert_array_equal(seq[3], exp["diag"])
+    np.testing.assert_array_equal(seq[4], exp["flags"])
+    np.testing.assert_array_equal(base, exp["base"])
+    np.testing.assert_array_equal(fwd, exp["fwd"])
+    if backward:
+        np.testing.assert_array_equal(bwd, exp["bwd"])
+    assert header[2] == exp["status"] == int(dev.status.item())
+    assert not counters.any()
+
+
+SETUP_CASES = [
+    ("cfg1", lambda: workloads.config1(causal=True)),
+    ("cfg3", lambda: workloads.config3()),
+    ("cfg4", lambda: workloads.config4(with_grad=True)),
+    ("cfg5_small", lambda: workloads.config5(doc_len=4096, chunk=512, offsets=(512, 3584))),
+] + [(f"random{s}", (lambda s=s: workloads.random_batch(s, batch=9, max_len=300,
+                                                         q_causal_offset=bool(s % 2))))
+     for s in range(100, 106)]
+
+
+@pytest.mark.parametrize("name,make", SETUP_CASES, ids=[c[0] for c in SETUP_CASES])
+@pytest.mark.parametrize("backward", [False, True])
+def test_setup_bit_exact(name, make, backward):
+    say(f"[setup] {name} backward={backward}")
+    _check_setup(make(), backward)
+
+
+# ------------------------------------------------------------------ small configs
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lse_kind", ["token", "head"])
+def test_config1_fwd_bwd(causal, lse_kind):
+    say(f"[cfg1] causal={causal} lse={lse_kind}")
+    batch = workloads.config1(causal=causal, lse_kind=lse_kind)
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+RANDOM = [(s, d) for s in range(200, 206) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("seed,dim", RANDOM)
+def test_random_fwd_bwd(seed, dim):
+    batch = workloads.random_batch(seed, batch=6, max_len=300, h_q=4, h_kv=2, dim=dim,
+                                   q_causal_offset=(seed % 3 == 0))
+    say(f"[random] seed={seed} D={dim} lq={batch.lq.tolist()} lk={batch.lk.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+def test_gqa_groups_of_four_fwd_bwd():
+    batch = workloads.random_batch(300, batch=4, max_len=200, h_q=8, h_kv=2, dim=128)
+    say(f"[gqa] lq={batch.lq.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+def test_aliased_kv_segments_sum_gradients():
+    batch = workloads.config5(doc_len=1024, chunk=256, offsets=(256, 768))
+    say("[alias] cfg5 shape, doc 1024 chunk 256")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+# ------------------------------------------------------------------ invariants on GPU
+
+def test_mixed_policy_equals_sum_of_two_passes_bitwise():
+    with open(os.path.join(GOLDEN, "mixed_policy_19row.json")) as f:
+        g = json.load(f)
+    one = g["single_call_reading"]
+    pol = [1 if p == "causal" else 0 for p in one["policies"]]
+    mixed = workloads.build("mixed19", 7, 2, 2, 64, one["lengths"], one["lengths"],
+                            one["start_rows"], one["start_rows"], default_policy=0, policy=pol,
+                            q_rows=19, kv_rows=19, with_grad=False)
+
+    def run(batch):
+        dev = _dev(batch, with_grad=False)
+        dev.flat["o"].view(torch.int16).zero_()
+        dev.fwd()
+        torch.cuda.synchronize()
+        return dev.host("o")
+
+    outs = []
+    for key, policy in (("causal_pass", 1), ("padding_pass", 0)):
+        lens = np.diff(g[key]["cu_seqlens"])
+        b = workloads.build("pass", 7, 2, 2, 64, lens, lens, g[key]["cu_seqlens_padded"],
+                            g[key]["cu_seqlens_padded"], default_policy=policy, q_rows=19,
+                            kv_rows=19, with_grad=False)
+        for n in ("q", "k", "v"):
+            b.data[n] = mixed.data[n]
+        outs.append(bf16_to_f64(run(b)))
+    m = bf16_to_f64(run(mixed))
+    np.testing.assert_array_equal(m, outs[0] + outs[1])
+
+
+def test_lse_layouts_agree_bitwise_and_forward_is_deterministic():
+    a = workloads.random_batch(400, batch=5, max_len=260, dim=128, lse_kind="token",
+                               with_grad=False)
+    b = workloads.random_batch(400, batch=5, max_len=260, dim=128, lse_kind="head",
+                               with_grad=False)
+    da, db = _dev(a), _dev(b)
+    da.fwd()
+    db.fwd()
+    torch.cuda.synchronize()
+    la = a.layouts["lse"].view(da.host("lse"))[:, :, 0]
+    lb = b.layouts["lse"].view(db.host("lse"))[:, :, 0]
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    assert np.array_equal(da.host("o"), db.host("o"))
+    first = da.host("o")
+    da.fwd()
+    torch.cuda.synchronize()
+    assert np.array_equal(first, da.host("o"))
+
+
+def test_bad_device_arguments_set_status_and_leave_outputs_untouched():
+    batch = workloads.random_batch(500, batch=4, max_len=100, zero_lengths=False,
+                                   token_gaps=False)
+    lay = batch.layouts["k"]
+    lay_q = batch.layouts["q"]
+    # sequence 1: K offset negative; sequence 2: Q offset past the span;
+    # sequence 3: policy 5
+    k_start = lay.start_rows.copy()
+    q_start = lay_q.start_rows.copy()
+    batch.layouts["k"].start_rows = k_start
+    dev = _dev(batch)
+    rk = dev.ragged["k"].clone()
+    rk[1] = -8
+    dev.ragged["k"] = rk
+    rq = dev.ragged["q"].clone()
+    rq[2] = lay_q.span
+    dev.ragged["q"] = rq
+    pol = dev.policy.clone()
+    pol[3] = 5
+    dev.policy = pol
+    dev.problem.mask_policy = pol
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    prob, t = oracle.from_batch(batch)
+    t["k"].ragged = rk.cpu().numpy()
+    t["q"].ragged = rq.cpu().numpy()
+    prob.policy = pol.cpu().numpy()
+    ref = oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"])
+    expected = oracle.ST_BAD_OFFSET | oracle.ST_OUT_OF_SPAN | oracle.ST_BAD_POLICY
+    assert ref["status"] == expected
+    assert int(dev.status.item()) == expected
+    compare_bf16(batch, "o", dev.host("o"), ref["o"], ref["o_written"], O_TOL)
+    bref = oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                           t["dk"], t["dv"])
+    for n in ("dq", "dk", "dv"):
+        compare_bf16(batch, n, dev.host(n), bref[n], bref[n + "_written"], GRAD_TOL)
+
+
+def test_workspace_guard_bands():
+    batch = workloads.random_batch(600, batch=5, max_len=300, dim=128)
+    dev = _dev(batch)
+    for backward in (False, True):
+        L = dev.bwd_layout() if backward else dev.fwd_layout()
+        guard = 4096
+        buf = torch.full((L.total_bytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        ws = buf[guard:guard + L.total_bytes]
+        if backward:
+            dev.bwd(workspace=ws)
+        else:
+            dev.fwd(workspace=ws)
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(host[:guard] == 0xA5) and np.all(host[-guard:] == 0xA5), \
+            f"workspace guard band overwritten (backward={backward})"
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+# ------------------------------------------------------------------ full-size configs
+
+def _sample_rows(batch, rng, n_seq=6, per_seq=4):
+    out = []
+    order = rng.permutation(batch.batch)[:n_seq]
+    for b in order:
+        lq = int(batch.lq[b])
+        if lq <= 0:
+            continue
+        rows = {0, lq - 1} | set(rng.integers(0, lq, size=per_seq - 2).tolist())
+        h = int(rng.integers(0, batch.h_q))
+        out.append((int(b), h, sorted(rows)))
+    return out
+
+
+def _check_sampled_fwd(batch, dev, seed):
+    rng = np.random.default_rng(seed)
+    prob, t = oracle.from_batch(batch)
+    o_gpu = batch.layouts["o"].view(dev.host("o"))
+    lse_gpu = batch.layouts["lse"].view(dev.host("lse"))[:, :, 0]
+    worst = 0.0
+    for b, h, rows in _sample_rows(batch, rng):
+        o_ref, l_ref = oracle.forward_rows(prob, t["q"], t["k"], t["v"], b, h, rows)
+        r0 = int(batch.layouts["o"].start_rows[b])
+        rl = int(batch.layouts["lse"].start_rows[b])
+        g = bf16_to_f64(o_gpu[np.asarray(rows) + r0, h])
+        err = np.abs(g - o_ref).max()
+        worst = max(worst, err)
+        assert err <= O_TOL, (b, h, rows, err)
+        np.testing.assert_allclose(lse_gpu[np.asarray(rows) + rl, h], l_ref, atol=1e-3, rtol=0)
+    return worst
+
+
+def _check_pads_untouched(batch, dev, names):
+    for n in names:
+        lay = batch.layouts[n]
+        valid = workloads.valid_rows(lay, batch.lq if n in ("o", "lse", "dq") else batch.lk)
+        got = lay.view(dev.host(n))
+        pre = lay.view(pre_fill(batch, n))
+        assert np.array_equal(got[~valid].view(np.uint8), pre[~valid].view(np.uint8)), n
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_forward_sampled(cfg):
+    batch = workloads.CONFIGS[cfg](with_grad=False)
+    say(f"[full fwd] config {cfg}: B={batch.batch} lq_sum={int(batch.lq.sum())}")
+    dev = _dev(batch, with_grad=False)
+    dev.fwd()
+    torch.cuda.synchronize()
+    assert int(dev.status.item()) == 0
+    _check_sampled_fwd(batch, dev, seed=cfg)
+    _check_pads_untouched(batch, dev, ("o", "lse"))
+
+
+@pytest.mark.parametrize("cfg,kv_heads", [(3, [0, 5]), (5, [3])])
+def test_full_size_backward_head_subset(cfg, kv_heads):
+    batch = workloads.CONFIGS[cfg](with_grad=True)
+    say(f"[full bwd] config {cfg} kv heads {kv_heads}")
+    dev = _dev(batch, with_grad=True)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    assert int(dev.status.item()) == 0
+    ref = oracle_bwd(batch, kv_heads=kv_heads)
+    for n in ("dq", "dk", "dv"):
+        w = ref[n + "_written"]
+        g = bf16_to_f64(dev.host(n)[w])
+        err = np.abs(g - ref[n][w]).max()
+        say(f"  {n}: max abs err {err:.3e} over {int(w.sum())} elements")
+        assert err <= GRAD_TOL
+    _check_pads_untouched(batch, dev, ("dq", "dk", "dv"))

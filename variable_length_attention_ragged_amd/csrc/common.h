@@ -1,0 +1,110 @@
+// Internal declarations shared by the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "varlen_attn.h"
+
+namespace vattn {
+
+// Tile sizes.  Forward: 4 waves x 32 query rows, 64-key K/V tiles.  Backward:
+// 4 waves x 32 key rows stay resident while 32-row query tiles stream past.
+constexpr int kFwdBlockM = 128;
+constexpr int kFwdBlockN = 64;
+constexpr int kBwdBlockM = 32;
+constexpr int kBwdBlockN = 128;
+constexpr int kQueues = 8;        // one claim queue per XCD (8 XCDs on MI355X)
+constexpr float kLog2eHost = 1.4426950408889634f;
+constexpr int kCounterWords = 64;
+
+enum TensorId { T_Q = 0, T_K, T_V, T_O, T_LSE, T_DO, T_DQ, T_DK, T_DV, T_COUNT };
+
+inline __host__ __device__ bool is_query_side(int id) {
+  return id == T_Q || id == T_O || id == T_LSE || id == T_DO || id == T_DQ;
+}
+
+// A tensor as the device sees it (strides and spans in elements).
+struct DevTensor {
+  int64_t span;
+  int64_t st;
+  int64_t sh;
+  const int64_t* ragged;
+  int32_t heads;
+  int32_t dim;     // D for bf16 tensors, 1 for LSE
+  int32_t align;   // required element alignment of ragged offsets
+  int32_t present;
+};
+
+// Pointers into one workspace, following varlen_attn_layout.
+struct WsView {
+  int32_t* counters;
+  int32_t* header;
+  int32_t* lq;
+  int32_t* lk;
+  int32_t* policy;
+  int32_t* diag;
+  int32_t* flags;
+  int64_t* base;        // [T_COUNT][batch]
+  int32_t* fwd_tiles;   // (b, t) pairs
+  int32_t* bwd_tiles;   // (first, members, u, max_lk) quadruples
+  char* scratch;
+  float* delta;
+  float* dq_accum;
+  int64_t fwd_cap;
+  int64_t bwd_cap;
+};
+
+struct SetupArgs {
+  int32_t batch, h_q, h_kv, head_dim;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int8_t* policy;
+  int32_t default_policy;
+  const int32_t* q_causal_offset;
+  DevTensor t[T_COUNT];
+  int32_t backward;
+  int32_t bm, bn, bm_b, bn_b;
+  WsView ws;
+  int32_t* dev_status;
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_st, lse_sh;
+  int32_t batch, h_q, h_kv, group;
+  float scale_log2;     // softmax scale * log2(e)
+  WsView ws;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, do_st, do_sh, lse_st, lse_sh;
+  int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
+  int32_t batch, h_q, h_kv, group;
+  float scale;
+  float scale_log2;
+  WsView ws;
+};
+
+// Kernel launchers (each enqueues on `stream` and returns the launch status).
+hipError_t launch_setup(const SetupArgs& a, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, hipStream_t stream);
+
+// Number of workgroups a persistent launch should use on the current device.
+int persistent_grid(const void* kernel, int threads, size_t lds_bytes);
+
+}  // namespace vattn

@@ -1,0 +1,261 @@
+// Forward kernel: ragged THD attention with softmax statistics (LSE).
+//
+// Work: one item = one tile of kFwdBlockM query rows of one sequence and one
+// query head.  Tiles come from the setup kernel's list; heads are mapped onto
+// XCD queues so that every query head sharing a K/V head is served by one XCD
+// (its L2 keeps that head's K/V).  Workgroups are persistent, claim items
+// from their own XCD's queue and then help the other queues.
+//
+// Per item (4 waves, 32 query rows each):
+//   S^T = K Q^T      MFMA 32x32x16 bf16, K from LDS, Q fragments in registers;
+//                    a lane owns one query row, so row max / row sum need one
+//                    swap between lane halves only;
+//   mask             key >= Lk, or key > row + diag for causal sequences;
+//   online softmax   exp2 with scale*log2(e) folded in;
+//   O^T += V^T P^T   MFMA, V read transposed from LDS (ds_read_b64_tr_b16),
+//                    P straight from the S^T accumulators (no data movement).
+// Rows past Lq load zeros and K/V rows past Lk are zero-filled in LDS: pad
+// rows are never read, so NaN pads cannot reach P@V (cudnn-frontend issue on
+// padded THD, "Interaction with #624": under padding every sequence's tail
+// tile would land in its own pad slot).  Output rows past Lq are not written.
+#include "common.h"
+#include "mfma_util.h"
+
+namespace vattn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int kPitch = D + 8;  // bf16 elements per LDS row (16-byte shift)
+  uint16_t k[kFwdBlockN * kPitch];
+  uint16_t v[kFwdBlockN * kPitch];
+};
+
+template <int D>
+__device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, int g) {
+  constexpr int BM = kFwdBlockM, BN = kFwdBlockN, P = FwdSmem<D>::kPitch;
+  constexpr int KS = D / 16;   // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;   // 32-wide blocks of head_dim
+  constexpr int CH = BN * D / 8 / kThreads;  // 16-byte chunks per thread per tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int B = a.batch;
+  const WsView& w = a.ws;
+
+  const int lq = w.lq[b], lk = w.lk[b], pol = w.policy[b];
+  const int64_t dg = w.diag[b];
+  const bool causal = pol != VARLEN_ATTN_PADDING;
+  const int64_t qbase = w.base[T_Q * B + b], kbase = w.base[T_K * B + b];
+  const int64_t vbase = w.base[T_V * B + b], obase = w.base[T_O * B + b];
+  const int64_t lbase = w.base[T_LSE * B + b];
+
+  const int q0 = t * BM;
+  const int rows = min(BM, lq - q0);
+  int kv_end = lk;
+  if (causal) kv_end = (int)min(max((int64_t)(q0 + rows) + dg, (int64_t)0), (int64_t)lk);
+  const int n_kv = (kv_end + BN - 1) / BN;
+
+  const int wq0 = q0 + wave * 32;
+  const bool wave_active = wq0 < lq;
+  int wave_kv_end = kv_end;
+  if (causal)
+    wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
+  const int i = wq0 + l32;
+  const bool row_ok = i < lq;
+  const int64_t row_limit = (int64_t)i + dg;  // last visible key for causal rows
+
+  // Q fragments (B operand of S^T): lane holds row i, dims 16ks + 8hf .. +7.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = a.q + qbase + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (row_ok) v = load16(qrow + 16 * ks);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  // K/V tile staging: registers hold the next tile while this one computes.
+  u32x4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + kThreads * c;
+      const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+      const int key = j * BN + row;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (key < lk) {
+        kv = load16(a.k + kbase + (int64_t)key * a.k_st + (int64_t)g * a.k_sh + col);
+        vv = load16(a.v + vbase + (int64_t)key * a.v_st + (int64_t)g * a.v_sh + col);
+      }
+      kreg[c] = kv;
+      vreg[c] = vv;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + kThreads * c;
+      const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+      store16(&sm.k[row * P + col], kreg[c]);
+      store16(&sm.v[row * P + col], vreg[c]);
+    }
+  };
+
+  if (n_kv > 0) load_tile(0);
+  for (int j = 0; j < n_kv; ++j) {
+    __syncthreads();  // the previous tile's readers are done
+    store_tile();
+    __syncthreads();
+    if (j + 1 < n_kv) load_tile(j + 1);
+    const int k0 = j * BN;
+    if (!wave_active || k0 >= wave_kv_end) continue;
+
+    // ---- S^T = K Q^T  (BN keys x 32 queries per wave)
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const uint16_t* krow = &sm.k[(kb * 32 + l32) * P + 8 * hf];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(as_bf16x8(load16(krow + 16 * ks)), qf[ks], s[kb]);
+    }
+
+    // ---- mask, scale, online softmax (lane = one query row)
+    const bool need_mask = (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * a.scale_log2;
+        if (need_mask) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= lk || (causal && (int64_t)key > row_limit)) x = -INFINITY;
+        }
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(s[kb][r] - m_use);
+        s[kb][r] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32);
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+
+    // P^T fragments: accumulator entries 8st..8st+7 of key block kb are the
+    // keys kb*32 + 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's row.
+    bf16x8 pf[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        pf[kb * 2 + st] = pack_bf16x8(s[kb][o], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
+                                      s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
+      }
+
+    // ---- O^T += V^T P^T: V fragment rows = the same key order as P.
+    const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = kb * 32 + 16 * st + 4 * hf + (li >> 2);
+          const s16x4 lo = lds_read_tr(&sm.v[r0 * P + col]);
+          const s16x4 hi = lds_read_tr(&sm.v[(r0 + 8) * P + col]);
+          acc[db] = mfma32(concat_bf16(lo, hi), pf[kb * 2 + st], acc[db]);
+        }
+    }
+  }
+
+  // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
+  if (row_ok) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = a.o + obase + (int64_t)i * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = db * 32 + 8 * rr + 4 * hf;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
+        pk[1] = pack_bf16x2(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
+        *(u32x2*)(orow + d) = pk;
+      }
+    if (hf == 0) {
+      const float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      a.lse[lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh] = lse;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+  __shared__ int s_item;
+  const WsView& w = a.ws;
+  const int n_tiles = w.header[0];
+  const int xcd = xcc_id() & (kQueues - 1);
+  const int group = a.group;
+  const int per_g = n_tiles * group;
+  for (int qi = 0; qi < kQueues; ++qi) {
+    const int qq = (xcd + qi) & (kQueues - 1);
+    const int n_g = qq < a.h_kv ? (a.h_kv - qq + kQueues - 1) / kQueues : 0;
+    const int n_items = n_g * per_g;
+    if (n_items == 0) continue;
+    for (;;) {
+      if (threadIdx.x == 0) s_item = atomicAdd(&w.counters[qq], 1);
+      __syncthreads();
+      const int j = s_item;
+      __syncthreads();
+      if (j >= n_items) break;
+      const int gi = j / per_g, rem = j - gi * per_g;
+      const int tile = rem / group, hh = rem - tile * group;
+      const int g = qq + kQueues * gi;
+      fwd_tile<D>(a, sm, w.fwd_tiles[2 * tile], w.fwd_tiles[2 * tile + 1], g * group + hh, g);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, hipStream_t stream) {
+  const void* k = head_dim == 64 ? (const void*)fwd_kernel<64> : (const void*)fwd_kernel<128>;
+  const int grid = persistent_grid(k, kThreads, 0);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vattn

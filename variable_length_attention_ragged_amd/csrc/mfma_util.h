@@ -1,0 +1,78 @@
+// gfx950 building blocks: bf16 vectors, MFMA, LDS transpose reads, XCD id.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.  Lane l holds
+// A[l%32][8*(l/32) + j] and B[8*(l/32) + j][l%32] for j = 0..7, and
+// D[8*(i/4) + 4*(l/32) + i%4][l%32] in acc[i] (verified on gfx950).
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane i names 4 consecutive bf16 at its address (a 16x4 matrix M,
+// row i); result lane i' receives M[4j + i'/4][i'%4] for j = 0..3.  Pointing
+// source lane i at row (r0 + i/4), column (c0 + 4*(i%4)) of a row-major tile
+// therefore hands lane i' the 4 rows r0..r0+3 of column c0 + i'.
+__device__ inline s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)(
+          (uintptr_t)p)));
+}
+
+__device__ inline bf16x8 concat_bf16(s16x4 lo, s16x4 hi) {
+  s16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ inline uint16_t to_bf16_bits(float a) {
+  __bf16 x = (__bf16)a;
+  return __builtin_bit_cast(uint16_t, x);
+}
+
+__device__ inline bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                     float a6, float a7) {
+  u32x4 r;
+  r[0] = pack_bf16x2(a0, a1);
+  r[1] = pack_bf16x2(a2, a3);
+  r[2] = pack_bf16x2(a4, a5);
+  r[3] = pack_bf16x2(a6, a7);
+  return as_bf16x8(r);
+}
+
+// XCD (accelerator complex die) executing this wave.
+__device__ inline int xcc_id() {
+  unsigned r;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(r));
+  return (int)(r & 0xf);
+}
+
+__device__ inline u32x4 load16(const uint16_t* p) { return *(const u32x4*)p; }
+__device__ inline void store16(uint16_t* p, u32x4 v) { *(u32x4*)p = v; }
+
+}  // namespace vattn

@@ -1,0 +1,263 @@
+// On-device setup: per-sequence metadata, validation and tile work lists.
+//
+// The caller's ragged offsets, lengths and policies are device data.  Reading
+// them on the host would need the device-to-host copy that the pages rule out
+// (cudnn-frontend issue on padded THD, "Proposal: consume the bound offsets on
+// device": the setup step already runs on device and can read the bound
+// offsets; validating device prefix sums on the host would need the read a
+// previous change removed).  So one workgroup reads them here, checks every
+// sequence against its tensors' spans, records one base per tensor (the
+// metadata widens beyond a single cu_q/cu_k pair, same section), and writes
+// the tile lists the compute kernels claim work from.  It also zeroes the
+// claim counters, which live in their own workspace region (cudnn-frontend
+// PR #462, "Root cause": an overrun clobbered the engine's tile counter).
+//
+// Ordering (this library's design): sequences by descending cost, ties by
+// index; a sequence's query tiles from last to first (causal tiles late in a
+// sequence see the most keys).  kv groups (consecutive sequences binding the
+// same K, V, dK, dV rows) likewise by descending cost.  Everything is integer
+// arithmetic and deterministic.
+#include "common.h"
+
+namespace vattn {
+namespace {
+
+constexpr int kSetupThreads = 1024;
+
+__device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ int check_tensor(const DevTensor& t, int64_t base, int64_t rows) {
+  if (base < 0 || (base % t.align) != 0) return VARLEN_ATTN_ST_BAD_OFFSET;
+  // The host guarantees (heads-1)*sh + dim <= span, so `extra` < span and
+  // nothing below overflows.
+  const int64_t extra = (int64_t)(t.heads - 1) * t.sh + (t.dim - 1);
+  const int64_t room = t.span - 1 - extra - base;  // offset the last row may start at
+  if (room < 0) return VARLEN_ATTN_ST_OUT_OF_SPAN;
+  return (rows - 1 > room / t.st) ? VARLEN_ATTN_ST_OUT_OF_SPAN : 0;
+}
+
+// Sum over the query tiles of max(1, number of key tiles the tile reaches).
+__device__ int64_t sequence_cost(int64_t lq, int64_t lk, bool causal, int64_t diag, int bm,
+                                 int bn) {
+  int64_t cost = 0;
+  const int64_t n = ceil_div64(lq, bm);
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t row_end = min(lq, (t + 1) * bm);
+    int64_t kv_end = lk;
+    if (causal) kv_end = min(max(row_end + diag, (int64_t)0), lk);
+    cost += max((int64_t)1, ceil_div64(kv_end, bn));
+  }
+  return cost;
+}
+
+// Exclusive block-wide scan of value(i) for i in [0, n) into out[i]; returns
+// the total.  Every thread of the block must call it.
+template <class F>
+__device__ int64_t block_exclusive_scan(int n, F value, int32_t* out) {
+  __shared__ int64_t buf[kSetupThreads];
+  __shared__ int64_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int c = 0; c < n; c += kSetupThreads) {
+    const int i = c + tid;
+    const int64_t v = (i < n) ? value(i) : 0;
+    buf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kSetupThreads; off <<= 1) {
+      const int64_t add = (tid >= off) ? buf[tid - off] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    const int64_t incl = buf[tid];
+    if (i < n) out[i] = (int32_t)(carry + incl - v);
+    __syncthreads();
+    if (tid == kSetupThreads - 1) carry += incl;
+    __syncthreads();
+  }
+  const int64_t total = carry;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  const WsView& w = a.ws;
+  __shared__ int s_status;
+  __shared__ int s_listed;
+  __shared__ int s_groups;
+  if (tid == 0) {
+    s_status = 0;
+    s_listed = 0;
+    s_groups = 0;
+  }
+  for (int i = tid; i < kCounterWords; i += kSetupThreads) w.counters[i] = 0;
+
+  // Scratch (64 bytes per sequence): int64 cost_f[B], cost_b[B], gcost[B];
+  // int32 order[B], pos[B], gfirst[B], gsize[B], glmax[B], gorder[B], gpos[B],
+  // gidx[B].
+  int64_t* cost_f = (int64_t*)w.scratch;
+  int64_t* cost_b = cost_f + B;
+  int64_t* gcost = cost_b + B;
+  int32_t* order = (int32_t*)(gcost + B);
+  int32_t* pos = order + B;
+  int32_t* gfirst = pos + B;
+  int32_t* gsize = gfirst + B;
+  int32_t* glmax = gsize + B;
+  int32_t* gorder = glmax + B;
+  int32_t* gpos = gorder + B;
+  int32_t* gidx = gpos + B;
+  __syncthreads();
+
+  // ---- per-sequence metadata and validation
+  for (int b = tid; b < B; b += kSetupThreads) {
+    const int64_t lq = (int64_t)a.cu_q[b + 1] - (int64_t)a.cu_q[b];
+    const int64_t lk = (int64_t)a.cu_kv[b + 1] - (int64_t)a.cu_kv[b];
+    const int pol = a.policy ? (int)a.policy[b] : a.default_policy;
+    int st = 0;
+    if (lq < 0 || lk < 0) st |= VARLEN_ATTN_ST_NEG_LENGTH;
+    if (pol < VARLEN_ATTN_PADDING || pol > VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT)
+      st |= VARLEN_ATTN_ST_BAD_POLICY;
+    for (int id = 0; id < T_COUNT; ++id) {
+      const DevTensor& t = a.t[id];
+      if (!t.present) continue;
+      const int64_t rows = is_query_side(id) ? lq : lk;
+      if (rows > 0) st |= check_tensor(t, t.ragged[b], rows);
+    }
+    const bool causal =
+        pol == VARLEN_ATTN_CAUSAL_TOP_LEFT || pol == VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT;
+    int64_t diag = 0;
+    if (causal) {
+      if (a.q_causal_offset)
+        diag = a.q_causal_offset[b];
+      else if (pol == VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT)
+        diag = lk - lq;
+    }
+    const bool valid = st == 0;
+    w.lq[b] = (int32_t)lq;
+    w.lk[b] = (int32_t)lk;
+    w.policy[b] = pol;
+    w.diag[b] = (int32_t)diag;
+    w.flags[b] = (valid ? 1 : 0) | (st << 8);
+    for (int id = 0; id < T_COUNT; ++id)
+      w.base[(int64_t)id * B + b] = a.t[id].present ? a.t[id].ragged[b] : 0;
+    cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, causal, diag, a.bm, a.bn) : 0;
+    cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, causal, diag, a.bm_b, a.bn_b) : 0;
+    if (st) atomicOr(&s_status, st);
+    if (valid && lq > 0) atomicAdd(&s_listed, 1);
+  }
+  __syncthreads();
+
+  // ---- forward tile list: rank listed sequences by (cost desc, index asc)
+  auto listed = [&](int b) { return (w.flags[b] & 1) && w.lq[b] > 0; };
+  for (int b = tid; b < B; b += kSetupThreads) {
+    if (!listed(b)) continue;
+    const int64_t cb = cost_f[b];
+    int r = 0;
+    for (int o = 0; o < B; ++o)
+      if (listed(o) && (cost_f[o] > cb || (cost_f[o] == cb && o < b))) ++r;
+    order[r] = b;
+  }
+  __syncthreads();
+  const int n_listed = s_listed;
+  const int bm = a.bm;
+  const int64_t n_fwd = block_exclusive_scan(
+      n_listed, [&](int r) { return ceil_div64(w.lq[order[r]], bm); }, pos);
+
+  // ---- backward kv groups
+  int64_t n_bwd = 0;
+  int n_groups = 0;
+  if (a.backward) {
+    auto member = [&](int b) { return (w.flags[b] & 1) && w.lk[b] > 0; };
+    auto same_kv = [&](int b0, int b1) {
+      return w.base[(int64_t)T_K * B + b0] == w.base[(int64_t)T_K * B + b1] &&
+             w.base[(int64_t)T_V * B + b0] == w.base[(int64_t)T_V * B + b1] &&
+             w.base[(int64_t)T_DK * B + b0] == w.base[(int64_t)T_DK * B + b1] &&
+             w.base[(int64_t)T_DV * B + b0] == w.base[(int64_t)T_DV * B + b1];
+    };
+    auto starts = [&](int b) {
+      return member(b) && !(b > 0 && member(b - 1) && same_kv(b - 1, b));
+    };
+    // group index of each group start = number of starts before it
+    const int64_t total_starts =
+        block_exclusive_scan(B, [&](int b) { return (int64_t)(starts(b) ? 1 : 0); }, gidx);
+    for (int b = tid; b < B; b += kSetupThreads) {
+      if (!starts(b)) continue;
+      const int g = gidx[b];
+      int n = 1;
+      int lmax = w.lk[b];
+      int64_t c = cost_b[b];
+      while (b + n < B && member(b + n) && same_kv(b, b + n)) {
+        lmax = max(lmax, w.lk[b + n]);
+        c += cost_b[b + n];
+        ++n;
+      }
+      gfirst[g] = b;
+      gsize[g] = n;
+      glmax[g] = lmax;
+      gcost[g] = c;
+    }
+    n_groups = (int)total_starts;
+    __syncthreads();
+    for (int g = tid; g < n_groups; g += kSetupThreads) {
+      const int64_t cg = gcost[g];
+      int r = 0;
+      for (int o = 0; o < n_groups; ++o)
+        if (gcost[o] > cg || (gcost[o] == cg && gfirst[o] < gfirst[g])) ++r;
+      gorder[r] = g;
+    }
+    __syncthreads();
+    const int bn_b = a.bn_b;
+    n_bwd = block_exclusive_scan(
+        n_groups, [&](int r) { return ceil_div64(glmax[gorder[r]], bn_b); }, gpos);
+  }
+
+  // ---- capacity check, then write the lists
+  const bool overflow = n_fwd > w.fwd_cap || (a.backward && n_bwd > w.bwd_cap);
+  if (!overflow) {
+    for (int r = tid; r < n_listed; r += kSetupThreads) {
+      const int b = order[r];
+      const int nt = (int)ceil_div64(w.lq[b], bm);
+      int32_t* dst = w.fwd_tiles + 2 * (int64_t)pos[r];
+      for (int k = 0; k < nt; ++k) {
+        dst[2 * k] = b;
+        dst[2 * k + 1] = nt - 1 - k;
+      }
+    }
+    if (a.backward) {
+      for (int r = tid; r < n_groups; r += kSetupThreads) {
+        const int g = gorder[r];
+        const int nt = (int)ceil_div64(glmax[g], a.bn_b);
+        int32_t* dst = w.bwd_tiles + 4 * (int64_t)gpos[r];
+        for (int u = 0; u < nt; ++u) {
+          dst[4 * u] = gfirst[g];
+          dst[4 * u + 1] = gsize[g];
+          dst[4 * u + 2] = u;
+          dst[4 * u + 3] = glmax[g];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int st = s_status;
+    if (overflow) st |= VARLEN_ATTN_ST_LIST_OVERFLOW;
+    w.header[0] = overflow ? 0 : (int32_t)n_fwd;
+    w.header[1] = overflow ? 0 : (int32_t)n_bwd;
+    w.header[2] = st;
+    w.header[3] = B;
+    for (int i = 4; i < 16; ++i) w.header[i] = 0;
+    if (st && a.dev_status) atomicOr(a.dev_status, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_setup(const SetupArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vattn

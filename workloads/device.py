@@ -1,0 +1,93 @@
+"""Device placement of a synthetic batch for the HIP library (no arithmetic).
+
+Copies the bytes of a ``workloads.Batch`` to the GPU, pre-fills output buffers
+with NaN payloads, and builds the library's ``Problem`` and ``Ragged``
+descriptors over the flat buffers with the batch's layouts.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import variable_length_attention_ragged_amd as va
+
+from . import BF16_OUT_NAN, F32_OUT_NAN, Batch
+
+OUTPUTS = ("o", "lse", "dq", "dk", "dv")
+
+
+class DeviceBatch:
+    def __init__(self, batch: Batch, device="cuda", with_grad: bool | None = None):
+        self.batch = batch
+        self.device = device
+        with_grad = ("do" in batch.data) if with_grad is None else with_grad
+        self.flat = {}
+        for n in ("q", "k", "v", "do"):
+            if n in batch.data:
+                self.flat[n] = torch.from_numpy(batch.data[n].view(np.int16)).to(device) \
+                    .view(torch.bfloat16)
+        names = ("o", "lse") + (("dq", "dk", "dv") if with_grad else ())
+        for n in names:
+            self.flat[n] = self.fresh_output(n)
+        self.ragged = {n: torch.from_numpy(lay.ragged.astype(np.int64)).to(device)
+                       for n, lay in batch.layouts.items()}
+        self.cu_q = torch.from_numpy(batch.cu_q).to(device)
+        self.cu_kv = torch.from_numpy(batch.cu_kv).to(device)
+        self.policy = None if batch.policy is None else torch.from_numpy(batch.policy).to(device)
+        self.qco = None if batch.q_causal_offset is None else \
+            torch.from_numpy(batch.q_causal_offset).to(device)
+        self.problem = va.Problem(self.cu_q, self.cu_kv, batch.h_q, batch.h_kv, batch.dim,
+                                  batch.scale, self.policy, batch.default_policy, self.qco)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def fresh_output(self, n: str) -> torch.Tensor:
+        lay = self.batch.layouts[n]
+        if n == "lse":
+            return torch.full((lay.span,), F32_OUT_NAN, dtype=torch.int32,
+                              device=self.device).view(torch.float32)
+        return torch.full((lay.span,), BF16_OUT_NAN, dtype=torch.int16,
+                          device=self.device).view(torch.bfloat16)
+
+    def rag(self, n: str) -> va.Ragged:
+        lay = self.batch.layouts[n]
+        flat = self.flat[n]
+        if n == "lse":
+            view = torch.as_strided(flat, (lay.rows, lay.heads), (lay.stride_t, lay.stride_h))
+        else:
+            view = torch.as_strided(flat, (lay.rows, lay.heads, lay.dim),
+                                    (lay.stride_t, lay.stride_h, 1))
+        return va.Ragged(view, self.ragged[n], span=lay.span)
+
+    def fwd(self, **kw):
+        return va.varlen_attn_fwd(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                  self.rag("o"), self.rag("lse"), dev_status=self.status, **kw)
+
+    def fwd_setup(self, **kw):
+        return va.varlen_attn_fwd_setup(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                        self.rag("o"), self.rag("lse"), dev_status=self.status,
+                                        **kw)
+
+    def bwd(self, **kw):
+        return va.varlen_attn_bwd(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                  self.rag("o"), self.rag("do"), self.rag("lse"), self.rag("dq"),
+                                  self.rag("dk"), self.rag("dv"), dev_status=self.status, **kw)
+
+    def bwd_setup(self, **kw):
+        return va.varlen_attn_bwd_setup(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                        self.rag("o"), self.rag("do"), self.rag("lse"),
+                                        self.rag("dq"), self.rag("dk"), self.rag("dv"),
+                                        dev_status=self.status, **kw)
+
+    def fwd_layout(self):
+        return va.varlen_attn_fwd_workspace_layout(self.problem, self.rag("o"))
+
+    def bwd_layout(self):
+        return va.varlen_attn_bwd_workspace_layout(self.problem, self.rag("lse"), self.rag("dq"),
+                                                   self.rag("dk"))
+
+    def host(self, n: str) -> np.ndarray:
+        """Raw host copy: uint16 bit patterns for bf16 buffers, float32 for LSE."""
+        t = self.flat[n]
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
