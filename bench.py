@@ -1,0 +1,231 @@
+"""Benchmark: ragged THD attention forward + backward on one MI355X.
+
+One step = one pass of the whole hot path over the packed causal workload
+(16 sequences with lengths U[128, 4096], seed 1002, H_q = H_kv = 32, D = 128,
+top-left causal, head-major LSE): setup + forward (O, LSE), then setup +
+dO.O preprocess + dK/dV (with dQ accumulation) + dQ finalize.  Inputs are
+resident in HBM before the timed region; workspaces are preallocated.
+
+Prints one JSON line.  ``value`` is causal-aware TFLOP/s of the whole step:
+forward 4*D*pairs and backward 10*D*pairs per head, pairs = allowed
+(query, key) pairs counted exactly from the drawn lengths.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def pairs_per_head(batch) -> np.ndarray:
+    """Allowed (query, key) pairs of each sequence, per head."""
+    out = np.zeros(batch.batch, np.int64)
+    for b in range(batch.batch):
+        lq, lk = int(batch.lq[b]), int(batch.lk[b])
+        pol = int(batch.policy[b]) if batch.policy is not None else batch.default_policy
+        if lq <= 0 or lk <= 0:
+            continue
+        if pol == 0:
+            out[b] = lq * lk
+            continue
+        if batch.q_causal_offset is not None:
+            d = int(batch.q_causal_offset[b])
+        else:
+            d = 0 if pol == 1 else lk - lq
+        i = np.arange(lq, dtype=np.int64)
+        out[b] = int(np.clip(i + d + 1, 0, lk).sum())
+    return out
+
+
+def fwd_bytes(batch) -> int:
+    """Compulsory HBM bytes of the forward: Q read + O write (valid rows),
+    K and V read once (distinct valid rows), LSE write."""
+    q_rows = int(batch.lq.sum())
+    kv_rows = int(batch.lk.sum())  # every workload here binds distinct K/V rows
+    if batch.name.startswith("long_context"):
+        kv_rows = int(batch.layouts["k"].rows)
+    D = batch.dim
+    return (2 * q_rows * batch.h_q * D * 2 + 2 * kv_rows * batch.h_kv * D * 2
+            + q_rows * batch.h_q * 4)
+
+
+def cpu_baseline(batch, target_s: float = 15.0):
+    """Time the fp64 oracle's forward, as it stands, on a bounded sample of the
+    same workload: every sequence for the first n query heads, n chosen from a
+    one-head probe so that the timed run takes about `target_s`."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    prob, t = oracle.from_batch(batch)
+    pairs = int(pairs_per_head(batch).sum())
+    t0 = time.perf_counter()
+    oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=[0])
+    probe = time.perf_counter() - t0
+    n = int(max(1, min(batch.h_q, round(target_s / max(probe, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=list(range(n)))
+    spent = time.perf_counter() - t0
+    flops = 4.0 * batch.dim * pairs * n
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward over all {batch.batch} sequences for {n} of "
+                      f"{batch.h_q} query heads ({flops / 1e9:.1f} GFLOP causal-aware, "
+                      f"{spent:.1f} s wall)"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times "
+                         "(calibrates HBM byte counters against a known size) and exit")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got "
+              f"--gpus {args.gpus}", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    from workloads.device import DeviceBatch
+    import variable_length_attention_ragged_amd as va
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    va.lib()
+    torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
+        return 0
+    batch = workloads.config2(with_grad=True)
+    dev = DeviceBatch(batch, with_grad=True)
+    fwd_ws = torch.empty(dev.fwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
+    bwd_ws = torch.empty(dev.bwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
+
+    pairs = int(pairs_per_head(batch).sum())
+    fwd_flops = 4.0 * batch.dim * batch.h_q * pairs
+    bwd_flops = 10.0 * batch.dim * batch.h_q * pairs
+
+    # One step, one event between consecutive kernels (all on the current
+    # stream, which the library launches on).
+    stages = [("setup (fwd)", lambda: dev.fwd_setup(workspace=fwd_ws)),
+              ("fwd_kernel", lambda: dev.fwd_stage("varlen_attn_fwd_attention", workspace=fwd_ws)),
+              ("setup (bwd)", lambda: dev.bwd_setup(workspace=bwd_ws)),
+              ("bwd_pre_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_preprocess",
+                                                       workspace=bwd_ws)),
+              ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws)),
+              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq_finalize",
+                                                      workspace=bwd_ws))]
+
+    def step(ev=None):
+        for n, (_, run) in enumerate(stages):
+            if ev is not None:
+                ev[n].record()
+            run()
+        if ev is not None:
+            ev[-1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(dev.status.item()) != 0:
+        print(f"device status {int(dev.status.item())}", file=sys.stderr)
+        return 1
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
+    stage_ms = {name: float(np.mean([e[n].elapsed_time(e[n + 1]) for e in evs]))
+                for n, (name, _) in enumerate(stages)}
+    fwd_kernel_ms = stage_ms["fwd_kernel"]
+    dkdv_ms = stage_ms["bwd_dkdv_kernel"]
+    bwd_ms = sum(v for k, v in stage_ms.items() if k.startswith("bwd") or k == "setup (bwd)")
+    fwd_ms = stage_ms["fwd_kernel"] + stage_ms["setup (fwd)"]
+    dominant = max(stage_ms, key=stage_ms.get)
+    kernel_flops = {"fwd_kernel": fwd_flops, "bwd_dkdv_kernel": bwd_flops}
+
+    fwd_tflops = fwd_flops / (fwd_kernel_ms * 1e-3) / 1e12
+    dom_tflops = kernel_flops.get(dominant, 0.0) / (stage_ms[dominant] * 1e-3) / 1e12
+    value = (fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "varlen attention fwd/bwd TFLOP/s (causal-aware) and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "packed causal THD: 16 sequences, lengths U[128,4096] (seed 1002), "
+                        "H_q=H_kv=32, D=128, top-left causal, head-major LSE; fwd+bwd",
+            "tokens": int(batch.lq.sum()),
+            "pairs_per_head": pairs,
+            "fwd_gflop": round(fwd_flops / 1e9, 2),
+            "bwd_gflop": round(bwd_flops / 1e9, 2),
+            "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "fwd_ms": round(fwd_ms, 4),
+            "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(fwd_tflops, 2),
+            "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+            "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_dkdv_tflops": round(bwd_flops / (dkdv_ms * 1e-3) / 1e12, 2),
+            "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "wall_s_timed": round(t_wall, 3),
+        },
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(dom_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -242,6 +242,43 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
                           void* stream);
 
+/* One stage at a time, for callers that schedule or time the stages
+ * themselves.  Each takes the same arguments as the full call, enqueues one
+ * kernel, and reads what the matching *_setup call (same arguments, earlier
+ * on the same stream, same workspace) wrote there.  The full calls are
+ * exactly: varlen_attn_fwd = fwd_setup, fwd_attention;
+ * varlen_attn_bwd = bwd_setup, bwd_preprocess, bwd_dkdv, bwd_dq_finalize.
+ *   fwd_attention    O and LSE of every listed tile
+ *   bwd_preprocess   delta = rowsum(dO * O) (fp32) and zeroed dq_accum rows
+ *   bwd_dkdv         dK, dV (bf16) and fp32 dQ partial sums in dq_accum
+ *   bwd_dq_finalize  dQ = scale * dq_accum (bf16) */
+int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                              const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                              const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                              void* stream);
+int varlen_attn_bwd_preprocess(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                               const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                               const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                               const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                               void* stream);
+int varlen_attn_bwd_dkdv(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                         const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                         const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                         const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                         const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                         void* stream);
+int varlen_attn_bwd_dq_finalize(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                                const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                                const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                                const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                                const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
+                                void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                                void* stream);
+
 /* Static text for a host return code. */
 const char* varlen_attn_status_string(int code);
 

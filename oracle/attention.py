@@ -99,9 +99,13 @@ class Tensor:
 
     def values(self) -> np.ndarray:
         """Buffer contents as float64 (bf16 bit patterns widened exactly)."""
+        return self.values_at(slice(None))
+
+    def values_at(self, idx) -> np.ndarray:
+        """Elements at `idx` as float64 (bf16 bit patterns widened exactly)."""
         if self.data.dtype == np.uint16:
-            return bf16_bits_to_f64(self.data)
-        return self.data.astype(np.float64)
+            return bf16_bits_to_f64(self.data[idx])
+        return self.data[idx].astype(np.float64)
 
 
 @dataclass
@@ -205,10 +209,11 @@ def _softmax_block(info: SeqInfo, scale: float, qb: np.ndarray, kb: np.ndarray, 
     return lse, p
 
 
-def _gather(vals: np.ndarray, t: Tensor, base: int, rows: int, head: int) -> np.ndarray:
+def _gather(t: Tensor, base: int, rows: int, head: int) -> np.ndarray:
+    """Rows [rows, dim] of one head of one sequence, widened to float64."""
     if rows <= 0:
         return np.zeros((0, t.dim))
-    return vals[t.index(base, rows, head)]
+    return t.values_at(t.index(base, rows, head))
 
 
 def forward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Tensor,
@@ -219,7 +224,6 @@ def forward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Tens
 
     ``heads``/``seqs`` restrict the work to a subset (sampling at full size);
     restricted outputs are only meaningful on the written elements."""
-    qv, kv_, vv = q.values(), k.values(), v.values()
     o_out, lse_out = o.values(), lse.values()
     o_w = np.zeros(o.span, bool)
     lse_w = np.zeros(lse.span, bool)
@@ -237,9 +241,9 @@ def forward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Tens
             for r0 in range(0, info.lq, ROW_BLOCK):
                 r1 = min(info.lq, r0 + ROW_BLOCK)
                 kl = _key_limit(info, r1)
-                qb = _gather(qv, q, int(q.ragged[b]) + r0 * q.stride_t, r1 - r0, h)
-                kb = _gather(kv_, k, int(k.ragged[b]), kl, g)
-                vb = _gather(vv, v, int(v.ragged[b]), kl, g)
+                qb = _gather(q, int(q.ragged[b]) + r0 * q.stride_t, r1 - r0, h)
+                kb = _gather(k, int(k.ragged[b]), kl, g)
+                vb = _gather(v, int(v.ragged[b]), kl, g)
                 lse_b, p = _softmax_block(info, prob.scale, qb, kb, r0)
                 ob = p @ vb if kl > 0 else np.zeros((r1 - r0, prob.head_dim))
                 oi = o.index(int(o.ragged[b]) + r0 * o.stride_t, r1 - r0, h)
@@ -258,14 +262,13 @@ def forward_rows(prob: Problem, q: Tensor, k: Tensor, v: Tensor, b: int, h: int,
     info = sequence_info(prob, [q], [k, v], b)
     rows = np.asarray(rows, np.int64)
     g = h // (prob.h_q // prob.h_kv)
-    qv, kv_, vv = q.values(), k.values(), v.values()
     out_o = np.zeros((rows.size, prob.head_dim))
     out_l = np.full(rows.size, -np.inf)
     for n, i in enumerate(rows):
         kl = _key_limit(info, int(i) + 1)
-        qi = qv[q.index(int(q.ragged[b]) + int(i) * q.stride_t, 1, h)]
-        kb = _gather(kv_, k, int(k.ragged[b]), kl, g)
-        vb = _gather(vv, v, int(v.ragged[b]), kl, g)
+        qi = _gather(q, int(q.ragged[b]) + int(i) * q.stride_t, 1, h)
+        kb = _gather(k, int(k.ragged[b]), kl, g)
+        vb = _gather(v, int(v.ragged[b]), kl, g)
         lse_i, p = _softmax_block(info, prob.scale, qi, kb, int(i))
         out_l[n] = lse_i[0]
         if kl > 0:
@@ -285,7 +288,6 @@ def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Ten
     to whole GQA groups.  ``o`` and ``lse`` (the forward's outputs, inputs of
     the backward) take part in the validation of each sequence only; the
     oracle recomputes both in fp64."""
-    qv, kv_, vv, dov = q.values(), k.values(), v.values(), do.values()
     dq_out, dk_out, dv_out = dq.values(), dk.values(), dv.values()
     dq_w = np.zeros(dq.span, bool)
     dk_w = np.zeros(dk.span, bool)
@@ -317,15 +319,15 @@ def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Ten
                     r1 = min(info.lq, r0 + ROW_BLOCK)
                     n = r1 - r0
                     kl = _key_limit(info, r1)
-                    qb = _gather(qv, q, int(q.ragged[b]) + r0 * q.stride_t, n, h)
-                    dob = _gather(dov, do, int(do.ragged[b]) + r0 * do.stride_t, n, h)
+                    qb = _gather(q, int(q.ragged[b]) + r0 * q.stride_t, n, h)
+                    dob = _gather(do, int(do.ragged[b]) + r0 * do.stride_t, n, h)
                     dqi = dq.index(int(dq.ragged[b]) + r0 * dq.stride_t, n, h)
                     dq_w[dqi] = True
                     if kl == 0:
                         dq_out[dqi] = 0.0
                         continue
-                    kb = _gather(kv_, k, int(k.ragged[b]), kl, g)
-                    vb = _gather(vv, v, int(v.ragged[b]), kl, g)
+                    kb = _gather(k, int(k.ragged[b]), kl, g)
+                    vb = _gather(v, int(v.ragged[b]), kl, g)
                     _, p = _softmax_block(info, prob.scale, qb, kb, r0)
                     ob = p @ vb
                     delta = (dob * ob).sum(axis=1)

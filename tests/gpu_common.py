@@ -9,9 +9,14 @@ import oracle
 import workloads
 from tests._util import bf16_to_f64
 
-# Tolerances (max-abs vs fp64) for the HIP path.
+# Tolerances (max-abs vs fp64) for the HIP path.  Gradients: 5e-2 absolute,
+# plus 2^-8 of the magnitude, because a bf16 output cannot come closer to the
+# exact value than half an ulp (2^-9 relative) and dS/P enter the bf16 MFMAs
+# rounded the same way; e.g. |dK| = 12 (many queries over few keys) has ulp
+# 0.0625.  For O(1) gradients the bar is the plain 5e-2.
 O_TOL = 2e-2
 GRAD_TOL = 5e-2
+GRAD_REL = 2.0 ** -8
 LSE_TOL = 1e-3
 
 
@@ -25,9 +30,9 @@ def pre_fill(batch: workloads.Batch, n: str) -> np.ndarray:
     return workloads.out_buffer(lay, "f32" if n == "lse" else "bf16")
 
 
-def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what=""):
-    """Written elements within `tol` of the oracle; all others bit-identical
-    to the pre-call contents."""
+def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what="", rel=0.0):
+    """Written elements within `tol + rel*|ref|` of the oracle; all others
+    bit-identical to the pre-call contents."""
     pre = pre_fill(batch, n)
     assert gpu_bits.shape == pre.shape
     untouched = ~written
@@ -38,9 +43,10 @@ def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what=""):
         r = ref_vals[written]
         assert np.all(np.isfinite(g)), f"{what}{n}: non-finite output in a valid row"
         err = np.abs(g - r)
-        assert err.max() <= tol, (f"{what}{n}: max abs err {err.max():.3e} > {tol} "
-                                  f"(at {np.argmax(err)}, gpu {g[np.argmax(err)]}, "
-                                  f"ref {r[np.argmax(err)]})")
+        excess = err - (tol + rel * np.abs(r))
+        worst = int(np.argmax(excess))
+        assert excess[worst] <= 0, (f"{what}{n}: abs err {err[worst]:.3e} > {tol} + {rel:.4f}"
+                                    f"*|ref| (at {worst}, gpu {g[worst]}, ref {r[worst]})")
         return float(err.max())
     return 0.0
 
@@ -85,5 +91,6 @@ def check_backward(batch, dev, ref=None, what=""):
     ref = oracle_bwd(batch) if ref is None else ref
     errs = {}
     for n in ("dq", "dk", "dv"):
-        errs[n] = compare_bf16(batch, n, dev.host(n), ref[n], ref[n + "_written"], GRAD_TOL, what)
+        errs[n] = compare_bf16(batch, n, dev.host(n), ref[n], ref[n + "_written"], GRAD_TOL, what,
+                               rel=GRAD_REL)
     return errs

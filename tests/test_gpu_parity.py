@@ -11,7 +11,7 @@ import torch
 import oracle
 import workloads
 from oracle import worklist
-from tests.gpu_common import (GRAD_TOL, O_TOL, check_backward, check_forward, compare_bf16,
+from tests.gpu_common import (GRAD_REL, GRAD_TOL, O_TOL, check_backward, check_forward, compare_bf16,
                               oracle_bwd, oracle_fwd, pre_fill, say)
 from tests._util import bf16_to_f64
 
@@ -231,7 +231,7 @@ def test_bad_device_arguments_set_status_and_leave_outputs_untouched():
     bref = oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
                            t["dk"], t["dv"])
     for n in ("dq", "dk", "dv"):
-        compare_bf16(batch, n, dev.host(n), bref[n], bref[n + "_written"], GRAD_TOL)
+        compare_bf16(batch, n, dev.host(n), bref[n], bref[n + "_written"], GRAD_TOL, rel=GRAD_REL)
 
 
 def test_workspace_guard_bands():
@@ -322,6 +322,7 @@ def test_full_size_backward_head_subset(cfg, kv_heads):
         w = ref[n + "_written"]
         g = bf16_to_f64(dev.host(n)[w])
         err = np.abs(g - ref[n][w]).max()
-        say(f"  {n}: max abs err {err:.3e} over {int(w.sum())} elements")
+        mag = np.abs(ref[n][w]).max()
+        say(f"  {n}: max abs err {err:.3e}, max |ref| {mag:.3e}, over {int(w.sum())} elements")
         assert err <= GRAD_TOL
     _check_pads_untouched(batch, dev, ("dq", "dk", "dv"))

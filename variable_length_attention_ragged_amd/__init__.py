@@ -23,7 +23,8 @@ from ._binding import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, PADDING, ST_BAD_OFF
 
 __all__ = [
     "Ragged", "Problem", "varlen_attn_fwd", "varlen_attn_bwd", "varlen_attn_fwd_setup",
-    "varlen_attn_bwd_setup", "varlen_attn_fwd_workspace_layout",
+    "varlen_attn_bwd_setup", "varlen_attn_fwd_attention", "varlen_attn_bwd_preprocess",
+    "varlen_attn_bwd_dkdv", "varlen_attn_bwd_dq_finalize", "varlen_attn_fwd_workspace_layout",
     "varlen_attn_bwd_workspace_layout", "varlen_attn_fwd_workspace_size",
     "varlen_attn_bwd_workspace_size", "status_string", "view_span", "PADDING",
     "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "ST_NEG_LENGTH", "ST_BAD_OFFSET",
@@ -187,3 +188,27 @@ def varlen_attn_bwd_setup(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged
     """Enqueue only the setup kernel of a backward call."""
     return _bwd_call("varlen_attn_bwd_setup", p, q, k, v, o, dout, lse, dq, dk, dv, workspace,
                      dev_status, stream)
+
+
+def varlen_attn_fwd_attention(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged,
+                              lse: Ragged, *, workspace: torch.Tensor,
+                              dev_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Enqueue only the forward kernel (the workspace must hold this call's setup)."""
+    return _fwd_call("varlen_attn_fwd_attention", p, q, k, v, o, lse, workspace, dev_status,
+                     stream)
+
+
+def _bwd_stage(name):
+    def run(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged, dout: Ragged, lse: Ragged,
+            dq: Ragged, dk: Ragged, dv: Ragged, *, workspace: torch.Tensor,
+            dev_status: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        return _bwd_call(name, p, q, k, v, o, dout, lse, dq, dk, dv, workspace, dev_status,
+                         stream)
+    run.__name__ = name
+    run.__doc__ = f"Enqueue only {name} (the workspace must hold this call's setup)."
+    return run
+
+
+varlen_attn_bwd_preprocess = _bwd_stage("varlen_attn_bwd_preprocess")
+varlen_attn_bwd_dkdv = _bwd_stage("varlen_attn_bwd_dkdv")
+varlen_attn_bwd_dq_finalize = _bwd_stage("varlen_attn_bwd_dq_finalize")

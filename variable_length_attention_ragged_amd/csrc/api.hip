@@ -209,7 +209,7 @@ int check_workspace(void* ws, size_t bytes, const varlen_attn_layout& L) {
 int run_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const varlen_attn_tensor* k,
             const varlen_attn_tensor* v, const varlen_attn_tensor* o,
             const varlen_attn_tensor* lse, void* ws, size_t ws_bytes, int32_t* dev_status,
-            void* stream, bool setup_only) {
+            void* stream, unsigned stages) {
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_tensor(q, p->h_q, p->head_dim, 2))) return rc;
@@ -231,8 +231,8 @@ int run_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   s.t[T_LSE] = dev_tensor(lse, p->h_q, 1, 1);
   s.ws = make_view((char*)ws, L, p->batch);
   s.dev_status = dev_status;
-  if (launch_setup(s, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
-  if (setup_only) return VARLEN_ATTN_OK;
+  if ((stages & STAGE_SETUP) && launch_setup(s, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
+  if (!(stages & STAGE_FWD)) return VARLEN_ATTN_OK;
   FwdArgs f;
   memset(&f, 0, sizeof(f));
   f.q = (const uint16_t*)q->data;
@@ -265,7 +265,7 @@ int run_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
             const varlen_attn_tensor* dout, const varlen_attn_tensor* lse,
             const varlen_attn_tensor* dq, const varlen_attn_tensor* dk,
             const varlen_attn_tensor* dv, void* ws, size_t ws_bytes, int32_t* dev_status,
-            void* stream, bool setup_only) {
+            void* stream, unsigned stages) {
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_tensor(q, p->h_q, p->head_dim, 2))) return rc;
@@ -295,8 +295,7 @@ int run_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   s.t[T_DV] = dev_tensor(dv, p->h_kv, p->head_dim, 8);
   s.ws = make_view((char*)ws, L, p->batch);
   s.dev_status = dev_status;
-  if (launch_setup(s, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
-  if (setup_only) return VARLEN_ATTN_OK;
+  if ((stages & STAGE_SETUP) && launch_setup(s, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
   BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.q = (const uint16_t*)q->data;
@@ -333,7 +332,12 @@ int run_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   a.scale = p->scale;
   a.scale_log2 = p->scale * kLog2eHost;
   a.ws = s.ws;
-  if (launch_bwd(a, p->head_dim, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
+  if ((stages & STAGE_BWD_PRE) && launch_bwd_pre(a, p->head_dim, st) != hipSuccess)
+    return VARLEN_ATTN_ERR_HIP;
+  if ((stages & STAGE_BWD_DKDV) && launch_bwd_dkdv(a, p->head_dim, st) != hipSuccess)
+    return VARLEN_ATTN_ERR_HIP;
+  if ((stages & STAGE_BWD_DQ) && launch_bwd_dq(a, p->head_dim, st) != hipSuccess)
+    return VARLEN_ATTN_ERR_HIP;
   return VARLEN_ATTN_OK;
 }
 
@@ -380,7 +384,8 @@ int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                     const varlen_attn_tensor* o, const varlen_attn_tensor* lse, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
-  return run_fwd(p, q, k, v, o, lse, workspace, workspace_bytes, dev_status, stream, false);
+  return run_fwd(p, q, k, v, o, lse, workspace, workspace_bytes, dev_status, stream,
+                 STAGE_SETUP | STAGE_FWD);
 }
 
 int varlen_attn_fwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
@@ -388,7 +393,15 @@ int varlen_attn_fwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
                           const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
                           void* stream) {
-  return run_fwd(p, q, k, v, o, lse, workspace, workspace_bytes, dev_status, stream, true);
+  return run_fwd(p, q, k, v, o, lse, workspace, workspace_bytes, dev_status, stream, STAGE_SETUP);
+}
+
+int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                              const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                              const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
+                              void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                              void* stream) {
+  return run_fwd(p, q, k, v, o, lse, workspace, workspace_bytes, dev_status, stream, STAGE_FWD);
 }
 
 int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
@@ -398,7 +411,7 @@ int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* dk, const varlen_attn_tensor* dv, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
   return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, dev_status,
-                 stream, false);
+                 stream, STAGE_SETUP | STAGE_BWD_PRE | STAGE_BWD_DKDV | STAGE_BWD_DQ);
 }
 
 int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
@@ -409,8 +422,23 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
                           void* stream) {
   return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, dev_status,
-                 stream, true);
+                 stream, STAGE_SETUP);
 }
+
+#define VATTN_BWD_STAGE(NAME, STAGE)                                                            \
+  int NAME(const varlen_attn_problem* p, const varlen_attn_tensor* q,                          \
+           const varlen_attn_tensor* k, const varlen_attn_tensor* v,                           \
+           const varlen_attn_tensor* o, const varlen_attn_tensor* dout,                        \
+           const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,                        \
+           const varlen_attn_tensor* dk, const varlen_attn_tensor* dv, void* workspace,         \
+           size_t workspace_bytes, int32_t* dev_status, void* stream) {                        \
+    return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,           \
+                   dev_status, stream, STAGE);                                                 \
+  }
+
+VATTN_BWD_STAGE(varlen_attn_bwd_preprocess, STAGE_BWD_PRE)
+VATTN_BWD_STAGE(varlen_attn_bwd_dkdv, STAGE_BWD_DKDV)
+VATTN_BWD_STAGE(varlen_attn_bwd_dq_finalize, STAGE_BWD_DQ)
 
 const char* varlen_attn_status_string(int code) {
   switch (code) {

@@ -323,19 +323,32 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  const int flat_grid = 4096;
+constexpr int kFlatGrid = 4096;
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
   if (head_dim == 64) {
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(flat_grid), dim3(kThreads), 0, stream, a);
     const int g = persistent_grid((const void*)bwd_dkdv_kernel<64>, kThreads, 0);
     hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(g), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(flat_grid), dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(flat_grid), dim3(kThreads), 0, stream, a);
     const int g = persistent_grid((const void*)bwd_dkdv_kernel<128>, kThreads, 0);
     hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(g), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(flat_grid), dim3(kThreads), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -102,7 +102,18 @@ struct BwdArgs {
 // Kernel launchers (each enqueues on `stream` and returns the launch status).
 hipError_t launch_setup(const SetupArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream);
+
+// Which kernels a call enqueues.
+enum Stage : unsigned {
+  STAGE_SETUP = 1u,
+  STAGE_FWD = 2u,
+  STAGE_BWD_PRE = 4u,
+  STAGE_BWD_DKDV = 8u,
+  STAGE_BWD_DQ = 16u,
+};
 
 // Number of workgroups a persistent launch should use on the current device.
 int persistent_grid(const void* kernel, int threads, size_t lds_bytes);

@@ -78,6 +78,15 @@ class DeviceBatch:
                                         self.rag("dq"), self.rag("dk"), self.rag("dv"),
                                         dev_status=self.status, **kw)
 
+    def fwd_stage(self, name: str, **kw):
+        return getattr(va, name)(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                 self.rag("o"), self.rag("lse"), dev_status=self.status, **kw)
+
+    def bwd_stage(self, name: str, **kw):
+        return getattr(va, name)(self.problem, self.rag("q"), self.rag("k"), self.rag("v"),
+                                 self.rag("o"), self.rag("do"), self.rag("lse"), self.rag("dq"),
+                                 self.rag("dk"), self.rag("dv"), dev_status=self.status, **kw)
+
     def fwd_layout(self):
         return va.varlen_attn_fwd_workspace_layout(self.problem, self.rag("o"))
 
