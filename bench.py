@@ -141,8 +141,7 @@ def main(argv=None) -> int:
               ("bwd_pre_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_preprocess",
                                                        workspace=bwd_ws)),
               ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws)),
-              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq_finalize",
-                                                      workspace=bwd_ws))]
+              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq", workspace=bwd_ws))]
 
     def step(ev=None):
         for n, (_, run) in enumerate(stages):
@@ -175,7 +174,11 @@ def main(argv=None) -> int:
     bwd_ms = sum(v for k, v in stage_ms.items() if k.startswith("bwd") or k == "setup (bwd)")
     fwd_ms = stage_ms["fwd_kernel"] + stage_ms["setup (fwd)"]
     dominant = max(stage_ms, key=stage_ms.get)
-    kernel_flops = {"fwd_kernel": fwd_flops, "bwd_dkdv_kernel": bwd_flops}
+    # Algorithmic work per kernel.  The backward's 10*D flops per pair are
+    # S, dP, dV, dK (dK/dV pass, 8*D) and dQ (dQ pass, 2*D); the dQ pass also
+    # recomputes S and dP, which is not counted as algorithmic work.
+    kernel_flops = {"fwd_kernel": fwd_flops, "bwd_dkdv_kernel": 0.8 * bwd_flops,
+                    "bwd_dq_kernel": 0.2 * bwd_flops}
 
     fwd_tflops = fwd_flops / (fwd_kernel_ms * 1e-3) / 1e12
     dom_tflops = kernel_flops.get(dominant, 0.0) / (stage_ms[dominant] * 1e-3) / 1e12
@@ -206,7 +209,8 @@ def main(argv=None) -> int:
             "fwd_tflops": round(fwd_tflops, 2),
             "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
             "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
-            "bwd_dkdv_tflops": round(bwd_flops / (dkdv_ms * 1e-3) / 1e12, 2),
+            "bwd_dkdv_tflops": round(0.8 * bwd_flops / (dkdv_ms * 1e-3) / 1e12, 2),
+            "bwd_dq_tflops": round(0.2 * bwd_flops / (stage_ms["bwd_dq_kernel"] * 1e-3) / 1e12, 2),
             "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "wall_s_timed": round(t_wall, 3),
         },

@@ -149,8 +149,8 @@ typedef struct varlen_attn_problem {
  *             tile of bwd_block_n key rows of a group of consecutive
  *             sequences that bind the same K, V, dK and dV rows
  *   scratch   setup kernel scratch
- *   delta     fp32, same element offsets as LSE (backward only)
- *   dq_accum  fp32, same element offsets as dQ (backward only) */
+ *   delta     fp32 rowsum(dO * O), same element offsets as LSE (backward
+ *             only) */
 typedef struct varlen_attn_layout {
   int64_t total_bytes;
   int64_t counters_offset;
@@ -164,8 +164,6 @@ typedef struct varlen_attn_layout {
   int64_t scratch_offset;
   int64_t delta_offset;
   int64_t delta_elems;
-  int64_t dq_accum_offset;
-  int64_t dq_accum_elems;
   int32_t fwd_block_m;
   int32_t fwd_block_n;
   int32_t bwd_block_m;
@@ -181,11 +179,10 @@ typedef struct varlen_attn_layout {
 int varlen_attn_fwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* o,
                                      varlen_attn_layout* out);
 
-/* Workspace layout of a backward call.  delta mirrors lse and dq_accum
- * mirrors dq element for element, so they are sized from the caller's spans
- * of those tensors, which count every axis (cudnn-frontend PR #462, "The fix
- * (commit 1)": size from every stride axis; a head-major [h, t] LSE needs
- * h*t elements, not t).  Host only. */
+/* Workspace layout of a backward call.  delta mirrors lse element for
+ * element, so it is sized from the caller's span of lse, which counts every
+ * axis (cudnn-frontend PR #462, "The fix (commit 1)": size from every stride
+ * axis; a head-major [h, t] LSE needs h*t elements, not t).  Host only. */
 int varlen_attn_bwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
                                      const varlen_attn_tensor* dq, const varlen_attn_tensor* dk,
                                      varlen_attn_layout* out);
@@ -247,11 +244,13 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
  * kernel, and reads what the matching *_setup call (same arguments, earlier
  * on the same stream, same workspace) wrote there.  The full calls are
  * exactly: varlen_attn_fwd = fwd_setup, fwd_attention;
- * varlen_attn_bwd = bwd_setup, bwd_preprocess, bwd_dkdv, bwd_dq_finalize.
+ * varlen_attn_bwd = bwd_setup, bwd_preprocess, bwd_dkdv, bwd_dq.
  *   fwd_attention    O and LSE of every listed tile
- *   bwd_preprocess   delta = rowsum(dO * O) (fp32) and zeroed dq_accum rows
- *   bwd_dkdv         dK, dV (bf16) and fp32 dQ partial sums in dq_accum
- *   bwd_dq_finalize  dQ = scale * dq_accum (bf16) */
+ *   bwd_preprocess   delta = rowsum(dO * O) (fp32, in the workspace)
+ *   bwd_dkdv         dK and dV (bf16), key-major: K/V resident, query tiles
+ *                    streamed
+ *   bwd_dq           dQ (bf16), query-major: Q/dO resident, K/V tiles
+ *                    streamed */
 int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                               const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
@@ -271,13 +270,13 @@ int varlen_attn_bwd_dkdv(const varlen_attn_problem* p, const varlen_attn_tensor*
                          const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
                          void* stream);
-int varlen_attn_bwd_dq_finalize(const varlen_attn_problem* p, const varlen_attn_tensor* q,
-                                const varlen_attn_tensor* k, const varlen_attn_tensor* v,
-                                const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
-                                const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
-                                const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
-                                void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                                void* stream);
+int varlen_attn_bwd_dq(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                       const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                       const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
+                       const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
+                       const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
+                       void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                       void* stream);
 
 /* Static text for a host return code. */
 const char* varlen_attn_status_string(int code);

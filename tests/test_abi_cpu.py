@@ -125,7 +125,7 @@ def test_head_major_stats_workspace_pin():
     L = _bwd_layout(lse, dq, dk)
     assert L.delta_elems == 58880
     assert L.delta_elems != g["token_stride_only_elems"]
-    assert L.dq_accum_offset - L.delta_offset >= 58880 * 4
+    assert L.total_bytes - L.delta_offset >= 58880 * 4
     # the view-based span the binding computes agrees
     import torch
     view = torch.empty(h, t).t()          # [t, h] view of head-major storage
@@ -139,9 +139,8 @@ def test_token_major_workspace_identities(T, h, d):
     dk = _t(T * h * d, h * d, d)
     L = _bwd_layout(lse, dq, dk, _p(batch=3, h_q=h, h_kv=h, d=d))
     assert L.delta_elems == T * h                 # softmax_sum = maxT * h_q
-    assert L.dq_accum_elems == T * h * d          # dQ_accum = maxT * h_q * d
-    assert L.total_bytes >= L.dq_accum_offset + 4 * T * h * d
-    assert L.delta_offset % 256 == 0 and L.dq_accum_offset % 256 == 0
+    assert L.total_bytes >= L.delta_offset + 4 * T * h
+    assert L.delta_offset % 256 == 0
 
 
 def test_regions_are_disjoint_and_ordered():
@@ -153,8 +152,7 @@ def test_regions_are_disjoint_and_ordered():
                (L.seq_offset, L.seq_i64_offset + 72 * 37),
                (L.fwd_tiles_offset, 8 * L.fwd_tiles_capacity),
                (L.bwd_tiles_offset, 16 * L.bwd_tiles_capacity),
-               (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems),
-               (L.dq_accum_offset, 4 * L.dq_accum_elems)]
+               (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems)]
     for (a, n), (b, _) in zip(regions, regions[1:]):
         assert a + n <= b and b % 256 == 0
     assert regions[-1][0] + regions[-1][1] <= L.total_bytes

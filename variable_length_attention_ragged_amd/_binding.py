@@ -40,7 +40,7 @@ class varlen_attn_layout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in (
         "total_bytes", "counters_offset", "header_offset", "seq_offset", "seq_i64_offset",
         "fwd_tiles_offset", "fwd_tiles_capacity", "bwd_tiles_offset", "bwd_tiles_capacity",
-        "scratch_offset", "delta_offset", "delta_elems", "dq_accum_offset", "dq_accum_elems")] + \
+        "scratch_offset", "delta_offset", "delta_elems")] + \
         [(n, c_int32) for n in ("fwd_block_m", "fwd_block_n", "bwd_block_m", "bwd_block_n")]
 
 
@@ -77,8 +77,8 @@ _SIGNATURES = {
                                    c_void_p, c_void_p],
     "varlen_attn_bwd_dkdv": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,
                              c_void_p, c_void_p],
-    "varlen_attn_bwd_dq_finalize": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,
-                                    c_void_p, c_void_p],
+    "varlen_attn_bwd_dq": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,
+                           c_void_p, c_void_p],
     "varlen_attn_status_string": [c_int],
 }
 

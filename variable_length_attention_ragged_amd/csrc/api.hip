@@ -104,7 +104,6 @@ void base_layout(int64_t B, int64_t fwd_cap, int64_t bwd_cap, varlen_attn_layout
   L->scratch_offset = off;
   off += align256(64 * B);
   L->delta_offset = off;
-  L->dq_accum_offset = off;
   L->total_bytes = off;
   L->fwd_block_m = kFwdBlockM;
   L->fwd_block_n = kFwdBlockN;
@@ -127,7 +126,6 @@ WsView make_view(char* ws, const varlen_attn_layout& L, int64_t B) {
   w.bwd_tiles = (int32_t*)(ws + L.bwd_tiles_offset);
   w.scratch = ws + L.scratch_offset;
   w.delta = (float*)(ws + L.delta_offset);
-  w.dq_accum = (float*)(ws + L.dq_accum_offset);
   w.fwd_cap = L.fwd_tiles_capacity;
   w.bwd_cap = L.bwd_tiles_capacity;
   return w;
@@ -174,9 +172,6 @@ int bwd_layout(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
   L->delta_offset = off;
   L->delta_elems = lse->span_elems;
   off += align256(lse->span_elems * 4);
-  L->dq_accum_offset = off;
-  L->dq_accum_elems = dq->span_elems;
-  off += align256(dq->span_elems * 4);
   L->total_bytes = off;
   return VARLEN_ATTN_OK;
 }
@@ -438,7 +433,7 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
 
 VATTN_BWD_STAGE(varlen_attn_bwd_preprocess, STAGE_BWD_PRE)
 VATTN_BWD_STAGE(varlen_attn_bwd_dkdv, STAGE_BWD_DKDV)
-VATTN_BWD_STAGE(varlen_attn_bwd_dq_finalize, STAGE_BWD_DQ)
+VATTN_BWD_STAGE(varlen_attn_bwd_dq, STAGE_BWD_DQ)
 
 const char* varlen_attn_status_string(int code) {
   switch (code) {

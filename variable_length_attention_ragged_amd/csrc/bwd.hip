@@ -1,25 +1,30 @@
-// Backward kernels: preprocess, dK/dV (+ dQ partials), dQ finalize.
+// Backward kernels: preprocess, dK/dV pass, dQ pass.
 //
-// The fp32 intermediates live in the workspace laid out on the user tensors'
-// own strides and ragged offsets: delta mirrors LSE and dq_accum mirrors dQ
-// element for element (the layout cudnn-frontend PR #462 describes for its
-// softmax_sum / dQ_accum, "Root cause"), which is why the workspace is sized
-// from the full spans of those tensors.
-//
-//   preprocess   delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32) and zero the
-//                valid rows of dq_accum;
-//   dkdv         per (kv group, 128-key tile, kv head): K and V stay resident
-//                (registers, and K also in LDS).  For every query head of the
-//                GQA group, every member sequence of the kv group (sequences
-//                binding the same K/V rows, e.g. context-parallel query
-//                chunks) and every 32-row query tile that can see the keys:
+//   preprocess   delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32).  delta lives
+//                in the workspace with the element offsets of LSE, as the
+//                softmax row-sum intermediate of cudnn-frontend PR #462 ("Root
+//                cause") lives on its user tensor's strides, which is why the
+//                workspace is sized from LSE's full span.
+//   dkdv         one item = (kv group, 128-key tile, kv head).  Each wave keeps
+//                32 keys of K and V in registers; 32-row query tiles of every
+//                query head of the GQA group and every member sequence of the
+//                kv group (sequences binding the same K/V rows) stream through
+//                LDS, double-buffered:
 //                  S = Q K^T, P = exp(S*scale - LSE) (0 where masked or dead),
-//                  dV += P^T dO, dP = dO V^T, dS = P o (dP - delta),
-//                  dK += dS^T Q, dq_accum += dS K  (fp32 atomics);
-//                then dK*scale and dV are written as bf16 for valid key rows;
-//   finalize     dQ = scale * dq_accum as bf16, valid rows only.
+//                  dP = dO V^T, dS = P o (dP - delta),
+//                  dV += P^T dO, dK += dS^T Q   (dO and Q read transposed);
+//                then dK*scale and dV are stored as bf16 for valid key rows.
+//   dq           one item = (128-row query tile, query head), K/V tiles of the
+//                causal band streaming through LDS like the forward:
+//                  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T o (dP^T - delta),
+//                  dQ^T += K^T dS^T  (K read transposed);
+//                dQ = scale * dQ stored as bf16 for valid rows.
+// dQ is accumulated in registers by a query-major pass instead of fp32
+// atomics from the key-major pass: that recomputes S and dP once more (14*D
+// flops per pair instead of 10*D) but writes every dQ element once.
 #include "common.h"
 #include "mfma_util.h"
+#include "tile_lds.h"
 
 namespace vattn {
 namespace {
@@ -42,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     const int b = w.fwd_tiles[2 * tile], t = w.fwd_tiles[2 * tile + 1];
     const int lq = w.lq[b];
     const int64_t obase = w.base[T_O * B + b], dobase = w.base[T_DO * B + b];
-    const int64_t lbase = w.base[T_LSE * B + b], dqbase = w.base[T_DQ * B + b];
+    const int64_t lbase = w.base[T_LSE * B + b];
     const int r_end = min(kFwdBlockM, lq - t * kFwdBlockM);
     for (int r = wave * RPP + lr; r < r_end; r += 4 * RPP) {
       const int64_t i = (int64_t)t * kFwdBlockM + r;
@@ -55,9 +60,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
       if (li == 0) w.delta[lbase + i * a.lse_st + (int64_t)h * a.lse_sh] = acc;
-      float* dqa = w.dq_accum + dqbase + i * a.dq_st + (int64_t)h * a.dq_sh + 8 * li;
-      *(f32x4*)dqa = f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(dqa + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -65,21 +67,21 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
 // ------------------------------------------------------------ dK / dV
 
 template <int D>
-struct BwdSmem {
-  static constexpr int kPitch = D + 8;
-  static constexpr int kSPitch = kBwdBlockN + 8;
-  uint16_t k[kBwdBlockN * kPitch];
-  uint16_t q[kBwdBlockM * kPitch];
-  uint16_t dout[kBwdBlockM * kPitch];
-  uint16_t ds[kBwdBlockM * kSPitch];
-  float lse2[kBwdBlockM];
-  float delta[kBwdBlockM];
+struct DkdvSmem {
+  uint16_t q[2][kBwdBlockM * D];
+  uint16_t dout[2][kBwdBlockM * D];
+  float lse[2][64];
+  float delta[2][64];
+};
+
+struct QPos {
+  int hh, mi, qs;
+  bool done;
 };
 
 template <int D>
-__device__ void dkdv_tile(const BwdArgs& a, BwdSmem<D>& sm, const int32_t* entry, int g) {
+__device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entry, int g) {
   constexpr int BM = kBwdBlockM, BN = kBwdBlockN;
-  constexpr int P = BwdSmem<D>::kPitch, SP = BwdSmem<D>::kSPitch;
   constexpr int KS = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
@@ -88,20 +90,15 @@ __device__ void dkdv_tile(const BwdArgs& a, BwdSmem<D>& sm, const int32_t* entry
 
   const int bfirst = entry[0], members = entry[1], u = entry[2], lmax = entry[3];
   const int k0 = u * BN;
+  const int wk0 = k0 + wave * 32;
+  const int my_key = wk0 + l32;
   const int64_t kbase = w.base[T_K * B + bfirst], vbase = w.base[T_V * B + bfirst];
   const int64_t dkbase = w.base[T_DK * B + bfirst], dvbase = w.base[T_DV * B + bfirst];
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // K tile into LDS (rows >= lmax zero), and this wave's K/V fragments
-  // (B operands: lane holds key k0 + 32*wave + l32, dims 16ks + 8hf .. +7).
-  __syncthreads();
-  for (int idx = tid; idx < BN * D / 8; idx += kThreads) {
-    const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-    const int key = k0 + row;
-    u32x4 v = {0, 0, 0, 0};
-    if (key < lmax) v = load16(a.k + kbase + (int64_t)key * a.k_st + (int64_t)g * a.k_sh + col);
-    store16(&sm.k[row * P + col], v);
-  }
-  const int my_key = k0 + wave * 32 + l32;
+  // K/V fragments (B operands): lane holds key my_key, dims 16ks + 8hf .. +7.
+  // A negative scale is folded into K for the score product only.
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -110,166 +107,172 @@ __device__ void dkdv_tile(const BwdArgs& a, BwdSmem<D>& sm, const int32_t* entry
       kv = load16(a.k + kbase + (int64_t)my_key * a.k_st + (int64_t)g * a.k_sh + 16 * ks + 8 * hf);
       vv = load16(a.v + vbase + (int64_t)my_key * a.v_st + (int64_t)g * a.v_sh + 16 * ks + 8 * hf);
     }
-    kf[ks] = as_bf16x8(kv);
+    kf[ks] = as_bf16x8(kv ^ flip);
     vf[ks] = as_bf16x8(vv);
   }
-  f32x16 dk[DB], dvacc[DB];
+  f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       dk[db][r] = 0.f;
-      dvacc[db][r] = 0.f;
+      dv[db][r] = 0.f;
     }
 
-  for (int mi = 0; mi < members; ++mi) {
+  // Query tiles to visit, in order: query heads of the group, member
+  // sequences, 32-row tiles from the first row that can see key k0.
+  auto first_row = [&](int mi, int& lo) -> bool {
     const int b = bfirst + mi;
-    const int lq = w.lq[b], lk = w.lk[b], pol = w.policy[b];
-    const int64_t dg = w.diag[b];
-    const bool causal = pol != VARLEN_ATTN_PADDING;
-    if (lq <= 0 || lk <= k0) continue;
-    int q_lo = 0;
-    if (causal) {
-      const int64_t first = (int64_t)k0 - dg;  // first row that can see key k0
-      if (first >= lq) continue;
-      q_lo = (int)max(first, (int64_t)0);
-      q_lo -= q_lo % BM;
+    const int lq = w.lq[b], lk = w.lk[b];
+    if (lq <= 0 || lk <= k0) return false;
+    lo = 0;
+    if (w.policy[b] != VARLEN_ATTN_PADDING) {
+      const int64_t first = (int64_t)k0 - w.diag[b];
+      if (first >= lq) return false;
+      lo = (int)max(first, (int64_t)0);
+      lo -= lo % BM;
     }
-    const int64_t qbase = w.base[T_Q * B + b], dobase = w.base[T_DO * B + b];
-    const int64_t lbase = w.base[T_LSE * B + b], dqbase = w.base[T_DQ * B + b];
-    for (int hh = 0; hh < a.group; ++hh) {
-      const int h = g * a.group + hh;
-      for (int qs = q_lo; qs < lq; qs += BM) {
-        __syncthreads();  // previous users of q/dout/ds are done
-        for (int idx = tid; idx < BM * D / 8; idx += kThreads) {
-          const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-          const int64_t i = qs + row;
-          u32x4 qv = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
-          if (i < lq) {
-            qv = load16(a.q + qbase + i * a.q_st + (int64_t)h * a.q_sh + col);
-            dv = load16(a.dout + dobase + i * a.do_st + (int64_t)h * a.do_sh + col);
-          }
-          store16(&sm.q[row * P + col], qv);
-          store16(&sm.dout[row * P + col], dv);
+    return true;
+  };
+  auto seek = [&](QPos p) -> QPos {
+    while (p.hh < a.group) {
+      while (p.mi < members) {
+        int lo;
+        if (first_row(p.mi, lo)) {
+          p.qs = lo;
+          return p;
         }
-        if (tid < BM) {
-          const int64_t i = qs + tid;
-          float l2 = INFINITY, dl = 0.f;
-          if (i < lq) {
-            const int64_t off = lbase + i * a.lse_st + (int64_t)h * a.lse_sh;
-            l2 = a.lse[off] * kLog2e;
-            dl = w.delta[off];
-          }
-          sm.lse2[tid] = l2;
-          sm.delta[tid] = dl;
-        }
-        __syncthreads();
+        ++p.mi;
+      }
+      p.mi = 0;
+      ++p.hh;
+    }
+    p.done = true;
+    return p;
+  };
+  auto next = [&](QPos p) -> QPos {
+    p.qs += BM;
+    if (p.qs < w.lq[bfirst + p.mi]) return p;
+    ++p.mi;
+    return seek(p);
+  };
+  auto issue = [&](const QPos& p, int buf) {
+    const int b = bfirst + p.mi, h = g * a.group + p.hh;
+    const int nrows = min(BM, w.lq[b] - p.qs);
+    const int64_t qs = p.qs;
+    issue_tile<D, BM>(a.q + w.base[T_Q * B + b] + qs * a.q_st + (int64_t)h * a.q_sh, nrows, a.q_st,
+                      sm.q[buf]);
+    issue_tile<D, BM>(a.dout + w.base[T_DO * B + b] + qs * a.do_st + (int64_t)h * a.do_sh, nrows,
+                      a.do_st, sm.dout[buf]);
+    const int64_t loff = w.base[T_LSE * B + b] + qs * a.lse_st + (int64_t)h * a.lse_sh;
+    if (wave == 0) issue_column(a.lse + loff, nrows, a.lse_st, sm.lse[buf]);
+    if (wave == 1) issue_column(w.delta + loff, nrows, a.lse_st, sm.delta[buf]);
+  };
 
-        // ---- S = Q K^T and dP = dO V^T (32 query rows x this wave's 32 keys)
-        f32x16 s, dp;
+  QPos cur = seek(QPos{0, 0, 0, false});
+  if (!cur.done) issue(cur, 0);
+  for (int n = 0; !cur.done; ++n) {
+    const int buf = n & 1;
+    const QPos nx = next(cur);
+    wait_tile_loads();
+    __syncthreads();  // tile n visible to all waves; tile n-1 fully consumed
+    if (!nx.done) issue(nx, buf ^ 1);
+
+    const int b = bfirst + cur.mi;
+    const int lq = w.lq[b], lk = w.lk[b];
+    const bool causal = w.policy[b] != VARLEN_ATTN_PADDING;
+    const int64_t dg = w.diag[b];
+    const int qs = cur.qs;
+    const bool skip = wk0 >= lk || (causal && (int64_t)wk0 > (int64_t)(qs + BM - 1) + dg);
+    if (!skip) {
+      const bool need_mask = qs + BM > lq || wk0 + 32 > lk ||
+                             (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
+      // ---- S = Q K^T and dP = dO V^T (32 queries x this wave's 32 keys).
+      // The accumulators start at the per-row terms, -LSE*log2(e)/c and
+      // -delta, so that afterwards s*c = S*scale*log2(e) - LSE*log2(e) and
+      // dp = dP - delta.  Entry r is query row 8*(r/4) + 4hf + r%4.
+      f32x16 s, dp;
+      const float inv_c = 1.f / c;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
-        const uint16_t* qrow = &sm.q[l32 * P + 8 * hf];
-        const uint16_t* drow = &sm.dout[l32 * P + 8 * hf];
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 x = *(const f32x4*)&sm.lse[buf][8 * rr + 4 * hf];
+        const f32x4 y = *(const f32x4*)&sm.delta[buf][8 * rr + 4 * hf];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(as_bf16x8(load16(qrow + 16 * ks)), kf[ks], s);
-          dp = mfma32(as_bf16x8(load16(drow + 16 * ks)), vf[ks], dp);
+        for (int e = 0; e < 4; ++e) {
+          s[4 * rr + e] = -x[e] * kLog2e * inv_c;
+          dp[4 * rr + e] = -y[e];
         }
-        // ---- P and dS; lane holds key my_key and query rows
-        //      8*(r/4) + 4hf + r%4 of the tile.
+      }
+      const uint16_t* qt = sm.q[buf];
+      const uint16_t* dt = sm.dout[buf];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int64_t qi = qs + qr;
-          bool ok = qi < lq && my_key < lk;
-          if (causal) ok = ok && (int64_t)my_key <= qi + dg;
-          const float p = ok ? exp2f(s[r] * a.scale_log2 - sm.lse2[qr]) : 0.f;
-          s[r] = p;
-          dp[r] = p * (dp[r] - sm.delta[qr]);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(as_bf16x8(load16(&qt[lds_off<D>(l32, 2 * ks + hf)])), kf[ks], s);
+        dp = mfma32(as_bf16x8(load16(&dt[lds_off<D>(l32, 2 * ks + hf)])), vf[ks], dp);
+      }
+      // ---- P and dS (lane: key my_key; entries: query rows)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(s[r] * c);
+        if (need_mask) {
+          const int q = qs + 8 * (r >> 2) + 4 * hf + (r & 3);
+          bool ok = q < lq && my_key < lk;
+          if (causal) ok = ok && (int64_t)my_key <= (int64_t)q + dg;
+          p = ok ? p : 0.f;
         }
-        // P^T / dS^T fragments: entries 8st..8st+7 are query rows
-        // 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's key.
-        bf16x8 pf[2], dsf[2];
+        s[r] = p;
+        dp[r] = p * dp[r];
+      }
+      // P^T / dS^T fragments: entries 8st..8st+7 are query rows
+      // 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's key.
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        pf[st] = pack_bf16x8(s[o], s[o + 1], s[o + 2], s[o + 3], s[o + 4], s[o + 5], s[o + 6],
+                             s[o + 7]);
+        dsf[st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4], dp[o + 5],
+                              dp[o + 6], dp[o + 7]);
+      }
+      // ---- dV += P^T dO, dK += dS^T Q (B operands read transposed from LDS)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);
+        const int e = 4 * (li & 1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int o = 8 * st;
-          pf[st] = pack_bf16x8(s[o], s[o + 1], s[o + 2], s[o + 3], s[o + 4], s[o + 5], s[o + 6],
-                               s[o + 7]);
-          dsf[st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4], dp[o + 5],
-                                dp[o + 6], dp[o + 7]);
-        }
-        // ---- dV += P^T dO, dK += dS^T Q (B operands read transposed from LDS)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int r0 = 16 * st + 4 * hf + (li >> 2);
-            const bf16x8 dob = concat_bf16(lds_read_tr(&sm.dout[r0 * P + col]),
-                                           lds_read_tr(&sm.dout[(r0 + 8) * P + col]));
-            const bf16x8 qb = concat_bf16(lds_read_tr(&sm.q[r0 * P + col]),
-                                          lds_read_tr(&sm.q[(r0 + 8) * P + col]));
-            dvacc[db] = mfma32(pf[st], dob, dvacc[db]);
-            dk[db] = mfma32(dsf[st], qb, dk[db]);
-          }
-        }
-        // ---- dS to LDS as [query][key] for the dQ product
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 8 * (r >> 2) + 4 * hf + (r & 3);
-          sm.ds[qr * SP + wave * 32 + l32] = to_bf16_bits(dp[r]);
-        }
-        __syncthreads();
-        // ---- dQ partial over the 128 keys: wave w owns head dims 32w..32w+31
-        if (wave < DB) {
-          f32x16 dq;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dq[r] = 0.f;
-          const int col = wave * 32 + 16 * (grp & 1) + 4 * (li & 3);
-#pragma unroll
-          for (int st = 0; st < BN / 16; ++st) {
-            const bf16x8 dsa = as_bf16x8(load16(&sm.ds[l32 * SP + 16 * st + 8 * hf]));
-            const int r0 = 16 * st + 8 * hf + (li >> 2);
-            const bf16x8 kb = concat_bf16(lds_read_tr(&sm.k[r0 * P + col]),
-                                          lds_read_tr(&sm.k[(r0 + 4) * P + col]));
-            dq = mfma32(dsa, kb, dq);
-          }
-          // dq[r] = dQ[query 8(r/4) + 4hf + r%4][dim 32w + l32]
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t qi = qs + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (qi < lq)
-              atomicAdd(w.dq_accum + dqbase + qi * a.dq_st + (int64_t)h * a.dq_sh + wave * 32 + l32,
-                        dq[r]);
-          }
+          const int r0 = 16 * st + 4 * hf + (li >> 2);
+          const bf16x8 dob = concat_bf16(lds_read_tr(&dt[lds_off<D>(r0, cl, e)]),
+                                         lds_read_tr(&dt[lds_off<D>(r0 + 8, cl, e)]));
+          const bf16x8 qb = concat_bf16(lds_read_tr(&qt[lds_off<D>(r0, cl, e)]),
+                                        lds_read_tr(&qt[lds_off<D>(r0 + 8, cl, e)]));
+          dv[db] = mfma32(pf[st], dob, dv[db]);
+          dk[db] = mfma32(dsf[st], qb, dk[db]);
         }
       }
     }
+    cur = nx;
   }
 
   // ---- dK * scale, dV as bf16 for key rows < lmax.  acc[r] holds
-  //      key 8(r/4) + 4hf + r%4 of this wave's 32, dim db*32 + l32.
+  //      key wk0 + 8(r/4) + 4hf + r%4, dim db*32 + l32.
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + wave * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int key = wk0 + 8 * (r >> 2) + 4 * hf + (r & 3);
       if (key < lmax) {
         const int d = db * 32 + l32;
         a.dk[dkbase + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + d] =
             to_bf16_bits(dk[db][r] * a.scale);
-        a.dv[dvbase + (int64_t)key * a.dv_st + (int64_t)g * a.dv_sh + d] = to_bf16_bits(dvacc[db][r]);
+        a.dv[dvbase + (int64_t)key * a.dv_st + (int64_t)g * a.dv_sh + d] = to_bf16_bits(dv[db][r]);
       }
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
   __shared__ int s_item;
   const WsView& w = a.ws;
   const int n_tiles = w.header[1];
@@ -281,42 +284,200 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (n_items == 0) continue;
     for (;;) {
       if (threadIdx.x == 0) s_item = atomicAdd(&w.counters[kQueues + qq], 1);
-      __syncthreads();
+      __syncthreads();  // also: every wave is done with the previous item's LDS
       const int j = s_item;
       __syncthreads();
       if (j >= n_items) break;
       const int gi = j / n_tiles, tile = j - gi * n_tiles;
-      dkdv_tile<D>(a, sm, w.bwd_tiles + 4 * tile, qq + kQueues * gi);
+      dkdv_item<D>(a, sm, w.bwd_tiles + 4 * tile, qq + kQueues * gi);
     }
   }
 }
 
-// ------------------------------------------------------------ finalize
+// ------------------------------------------------------------ dQ
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;
-  constexpr int RPP = 64 / LPR;
-  const WsView& w = a.ws;
+struct DqSmem {
+  uint16_t k[2][kFwdBlockN * D];
+  uint16_t v[2][kFwdBlockN * D];
+};
+
+template <int D>
+__device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, int g) {
+  constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
+  constexpr int KS = D / 16, DB = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
-  const int n_items = w.header[0] * a.h_q;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane % LPR, lr = lane / LPR;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = item / a.h_q, h = item - tile * a.h_q;
-    const int b = w.fwd_tiles[2 * tile], t = w.fwd_tiles[2 * tile + 1];
-    const int lq = w.lq[b];
-    const int64_t dqbase = w.base[T_DQ * B + b];
-    const int r_end = min(kFwdBlockM, lq - t * kFwdBlockM);
-    for (int r = wave * RPP + lr; r < r_end; r += 4 * RPP) {
-      const int64_t i = (int64_t)t * kFwdBlockM + r;
-      const int64_t off = dqbase + i * a.dq_st + (int64_t)h * a.dq_sh + 8 * li;
-      const f32x4 x0 = *(const f32x4*)(w.dq_accum + off);
-      const f32x4 x1 = *(const f32x4*)(w.dq_accum + off + 4);
-      const bf16x8 y = pack_bf16x8(x0[0] * a.scale, x0[1] * a.scale, x0[2] * a.scale,
-                                   x0[3] * a.scale, x1[0] * a.scale, x1[1] * a.scale,
-                                   x1[2] * a.scale, x1[3] * a.scale);
-      store16(a.dq + off, __builtin_bit_cast(u32x4, y));
+  const WsView& w = a.ws;
+
+  const int lq = w.lq[b], lk = w.lk[b];
+  const int64_t dg = w.diag[b];
+  const bool causal = w.policy[b] != VARLEN_ATTN_PADDING;
+  const int64_t qbase = w.base[T_Q * B + b], dobase = w.base[T_DO * B + b];
+  const int64_t kbase = w.base[T_K * B + b], vbase = w.base[T_V * B + b];
+  const int64_t lbase = w.base[T_LSE * B + b], dqbase = w.base[T_DQ * B + b];
+
+  const int q0 = t * BM;
+  const int rows = min(BM, lq - q0);
+  int kv_end = lk;
+  if (causal) kv_end = (int)min(max((int64_t)(q0 + rows) + dg, (int64_t)0), (int64_t)lk);
+  const int n_kv = (kv_end + BN - 1) / BN;
+  const int wq0 = q0 + wave * 32;
+  const bool wave_active = wq0 < lq;
+  int wave_kv_end = kv_end;
+  if (causal)
+    wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
+  const int i = wq0 + l32;
+  const bool row_ok = i < lq;
+  const int64_t row_limit = (int64_t)i + dg;
+
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+
+  // Q (sign folded as in the forward) and dO fragments: row i, dims 16ks + 8hf.
+  bf16x8 qf[KS], df[KS];
+  float s_init = 0.f, dl = 0.f;
+  {
+    const uint16_t* qrow = a.q + qbase + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * hf;
+    const uint16_t* drow = a.dout + dobase + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 qv = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
+      if (row_ok) {
+        qv = load16(qrow + 16 * ks);
+        dv = load16(drow + 16 * ks);
+      }
+      qf[ks] = as_bf16x8(qv ^ flip);
+      df[ks] = as_bf16x8(dv);
+    }
+    if (row_ok) {
+      const int64_t off = lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh;
+      s_init = -a.lse[off] * kLog2e / c;
+      dl = w.delta[off];
+    }
+  }
+
+  const uint16_t* khead = a.k + kbase + (int64_t)g * a.k_sh;
+  const uint16_t* vhead = a.v + vbase + (int64_t)g * a.v_sh;
+  auto load_kv = [&](int j, int buf) {
+    const int k0 = j * BN;
+    const int nrows = min(BN, lk - k0);
+    issue_tile<D, BN>(khead + (int64_t)k0 * a.k_st, nrows, a.k_st, sm.k[buf]);
+    issue_tile<D, BN>(vhead + (int64_t)k0 * a.v_st, nrows, a.v_st, sm.v[buf]);
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  if (n_kv > 0) load_kv(0, 0);
+  for (int j = 0; j < n_kv; ++j) {
+    const int buf = j & 1;
+    wait_tile_loads();
+    __syncthreads();
+    if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
+    const int k0 = j * BN;
+    if (!wave_active || k0 >= wave_kv_end) continue;
+    const uint16_t* kt = sm.k[buf];
+    const uint16_t* vt = sm.v[buf];
+
+    // ---- per 32-key block: S^T = K Q^T and dP^T = V dO^T, then
+    //      dS^T = P^T o (dP^T - delta).  The accumulators start at the row
+    //      terms (-LSE*log2(e)/c and -delta) so no separate subtraction is
+    //      needed.  Lane: query row i; entry r: key 8*(r/4) + 4hf + r%4.
+    const bool need_mask =
+        (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
+    bf16x8 dsf[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = s_init;
+        dp[r] = -dl;
+      }
+      const int row = kb * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(as_bf16x8(load16(&kt[lds_off<D>(row, 2 * ks + hf)])), qf[ks], s);
+        dp = mfma32(as_bf16x8(load16(&vt[lds_off<D>(row, 2 * ks + hf)])), df[ks], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(s[r] * c);
+        if (need_mask) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool ok = key < lk && !(causal && (int64_t)key > row_limit);
+          p = ok ? p : 0.f;
+        }
+        dp[r] = p * dp[r];
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        dsf[kb * 2 + st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4],
+                                       dp[o + 5], dp[o + 6], dp[o + 7]);
+      }
+    }
+    // ---- dQ^T += K^T dS^T: K read transposed, keys in the order of dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);
+      const int e = 4 * (li & 1);
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = kb * 32 + 16 * st + 4 * hf + (li >> 2);
+          const s16x4 lo = lds_read_tr(&kt[lds_off<D>(r0, cl, e)]);
+          const s16x4 hi = lds_read_tr(&kt[lds_off<D>(r0 + 8, cl, e)]);
+          acc[db] = mfma32(concat_bf16(lo, hi), dsf[kb * 2 + st], acc[db]);
+        }
+    }
+  }
+
+  if (row_ok) {
+    uint16_t* qrow = a.dq + dqbase + (int64_t)i * a.dq_st + (int64_t)h * a.dq_sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d = db * 32 + 8 * rr + 4 * hf;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[db][4 * rr] * a.scale, acc[db][4 * rr + 1] * a.scale);
+        pk[1] = pack_bf16x2(acc[db][4 * rr + 2] * a.scale, acc[db][4 * rr + 3] * a.scale);
+        *(u32x2*)(qrow + d) = pk;
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  __shared__ int s_item;
+  const WsView& w = a.ws;
+  const int n_tiles = w.header[0];
+  const int xcd = xcc_id() & (kQueues - 1);
+  const int group = a.group;
+  const int per_g = n_tiles * group;
+  for (int qi = 0; qi < kQueues; ++qi) {
+    const int qq = (xcd + qi) & (kQueues - 1);
+    const int n_g = qq < a.h_kv ? (a.h_kv - qq + kQueues - 1) / kQueues : 0;
+    const int n_items = n_g * per_g;
+    if (n_items == 0) continue;
+    for (;;) {
+      if (threadIdx.x == 0) s_item = atomicAdd(&w.counters[2 * kQueues + qq], 1);
+      __syncthreads();
+      const int j = s_item;
+      __syncthreads();
+      if (j >= n_items) break;
+      const int gi = j / per_g, rem = j - gi * per_g;
+      const int tile = rem / group, hh = rem - tile * group;
+      const int g = qq + kQueues * gi;
+      dq_tile<D>(a, sm, w.fwd_tiles[2 * tile], w.fwd_tiles[2 * tile + 1], g * group + hh, g);
     }
   }
 }
@@ -345,10 +506,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+  if (head_dim == 64) {
+    const int g = persistent_grid((const void*)bwd_dq_kernel<64>, kThreads, 0);
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(g), dim3(kThreads), 0, stream, a);
+  } else {
+    const int g = persistent_grid((const void*)bwd_dq_kernel<128>, kThreads, 0);
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

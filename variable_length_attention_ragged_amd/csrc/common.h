@@ -8,8 +8,9 @@
 
 namespace vattn {
 
-// Tile sizes.  Forward: 4 waves x 32 query rows, 64-key K/V tiles.  Backward:
-// 4 waves x 32 key rows stay resident while 32-row query tiles stream past.
+// Tile sizes.  Forward and dQ pass: 4 waves x 32 query rows, 64-key K/V
+// tiles.  dK/dV pass: 4 waves x 32 key rows stay resident while 32-row query
+// tiles stream past.
 constexpr int kFwdBlockM = 128;
 constexpr int kFwdBlockN = 64;
 constexpr int kBwdBlockM = 32;
@@ -50,7 +51,6 @@ struct WsView {
   int32_t* bwd_tiles;   // (first, members, u, max_lk) quadruples
   char* scratch;
   float* delta;
-  float* dq_accum;
   int64_t fwd_cap;
   int64_t bwd_cap;
 };

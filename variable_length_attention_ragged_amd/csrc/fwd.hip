@@ -7,19 +7,23 @@
 // from their own XCD's queue and then help the other queues.
 //
 // Per item (4 waves, 32 query rows each):
-//   S^T = K Q^T      MFMA 32x32x16 bf16, K from LDS, Q fragments in registers;
-//                    a lane owns one query row, so row max / row sum need one
-//                    swap between lane halves only;
-//   mask             key >= Lk, or key > row + diag for causal sequences;
-//   online softmax   exp2 with scale*log2(e) folded in;
+//   K/V tiles        64 keys, double-buffered in LDS, loaded with buffer
+//                    loads straight into LDS; key rows past Lk lie outside the
+//                    buffer resource's range and arrive as zeros, so pad rows
+//                    are never read (cudnn-frontend issue on padded THD,
+//                    "Interaction with #624": under padding every sequence's
+//                    tail tile would otherwise land in its own pad slot);
+//   S^T = K Q^T      MFMA 32x32x16 bf16, Q fragments in registers; a lane
+//                    owns one query row, so the row max needs one swap between
+//                    lane halves and the row sum none until the end;
+//   online softmax   max on raw scores, exp2(fma(s, scale*log2e, -m)),
+//                    accumulators rescaled only when some row's max grew;
 //   O^T += V^T P^T   MFMA, V read transposed from LDS (ds_read_b64_tr_b16),
-//                    P straight from the S^T accumulators (no data movement).
-// Rows past Lq load zeros and K/V rows past Lk are zero-filled in LDS: pad
-// rows are never read, so NaN pads cannot reach P@V (cudnn-frontend issue on
-// padded THD, "Interaction with #624": under padding every sequence's tail
-// tile would land in its own pad slot).  Output rows past Lq are not written.
+//                    P taken straight from the S^T accumulators.
+// Query rows past Lq load zeros and are never stored.
 #include "common.h"
 #include "mfma_util.h"
+#include "tile_lds.h"
 
 namespace vattn {
 namespace {
@@ -28,19 +32,17 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int kPitch = D + 8;  // bf16 elements per LDS row (16-byte shift)
-  uint16_t k[kFwdBlockN * kPitch];
-  uint16_t v[kFwdBlockN * kPitch];
+  uint16_t k[2][kFwdBlockN * D];
+  uint16_t v[2][kFwdBlockN * D];
 };
 
 template <int D>
 __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, int g) {
-  constexpr int BM = kFwdBlockM, BN = kFwdBlockN, P = FwdSmem<D>::kPitch;
+  constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-wide blocks of head_dim
-  constexpr int CH = BN * D / 8 / kThreads;  // 16-byte chunks per thread per tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hf = lane >> 5, l32 = lane & 31;
+  const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
   const WsView& w = a.ws;
 
@@ -64,7 +66,12 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
   const int i = wq0 + l32;
   const bool row_ok = i < lq;
-  const int64_t row_limit = (int64_t)i + dg;  // last visible key for causal rows
+  const int64_t row_limit = (int64_t)i + dg;  // last visible key of a causal row
+
+  // A negative scale is folded into Q (exact sign flip) so that the row max
+  // can be taken on raw scores and c > 0.
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);  // scale 0: uniform weights, no 0*inf
+  const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q fragments (B operand of S^T): lane holds row i, dims 16ks + 8hf .. +7.
   bf16x8 qf[KS];
@@ -74,52 +81,38 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0, 0, 0, 0};
       if (row_ok) v = load16(qrow + 16 * ks);
+      v ^= flip;
       qf[ks] = as_bf16x8(v);
     }
   }
 
-  float m = -INFINITY, l = 0.f;
+  // One tile of K and V (rows k0..k0+BN-1 of kv head g) into buffer `buf`.
+  const uint16_t* khead = a.k + kbase + (int64_t)g * a.k_sh;
+  const uint16_t* vhead = a.v + vbase + (int64_t)g * a.v_sh;
+  auto load_kv = [&](int j, int buf) {
+    const int k0 = j * BN;
+    const int nrows = min(BN, lk - k0);
+    issue_tile<D, BN>(khead + (int64_t)k0 * a.k_st, nrows, a.k_st, sm.k[buf]);
+    issue_tile<D, BN>(vhead + (int64_t)k0 * a.v_st, nrows, a.v_st, sm.v[buf]);
+  };
+
+  float m = -INFINITY, l = 0.f;  // l: this lane's half of the row sum
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  // K/V tile staging: registers hold the next tile while this one computes.
-  u32x4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + kThreads * c;
-      const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-      const int key = j * BN + row;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (key < lk) {
-        kv = load16(a.k + kbase + (int64_t)key * a.k_st + (int64_t)g * a.k_sh + col);
-        vv = load16(a.v + vbase + (int64_t)key * a.v_st + (int64_t)g * a.v_sh + col);
-      }
-      kreg[c] = kv;
-      vreg[c] = vv;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = tid + kThreads * c;
-      const int row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-      store16(&sm.k[row * P + col], kreg[c]);
-      store16(&sm.v[row * P + col], vreg[c]);
-    }
-  };
-
-  if (n_kv > 0) load_tile(0);
+  if (n_kv > 0) load_kv(0, 0);
   for (int j = 0; j < n_kv; ++j) {
-    __syncthreads();  // the previous tile's readers are done
-    store_tile();
-    __syncthreads();
-    if (j + 1 < n_kv) load_tile(j + 1);
+    const int buf = j & 1;
+    wait_tile_loads();  // this wave's part of tile j landed
+    __syncthreads();    // all parts of tile j visible; tile j-1 fully consumed
+    if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
     const int k0 = j * BN;
     if (!wave_active || k0 >= wave_kv_end) continue;
+    const uint16_t* ks_ = sm.k[buf];
+    const uint16_t* vs_ = sm.v[buf];
 
     // ---- S^T = K Q^T  (BN keys x 32 queries per wave)
     f32x16 s[BN / 32];
@@ -127,46 +120,50 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const uint16_t* krow = &sm.k[(kb * 32 + l32) * P + 8 * hf];
+      const int row = kb * 32 + l32;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(as_bf16x8(load16(krow + 16 * ks)), qf[ks], s[kb]);
+      for (int ks = 0; ks < KS; ++ks)
+        s[kb] = mfma32(as_bf16x8(load16(&ks_[lds_off<D>(row, 2 * ks + hf)])), qf[ks], s[kb]);
     }
 
-    // ---- mask, scale, online softmax (lane = one query row)
-    const bool need_mask = (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
+    // ---- mask (boundary tiles only), row max on raw scores
+    const bool need_mask =
+        (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= lk || (causal && (int64_t)key > row_limit)) s[kb][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= lk || (causal && (int64_t)key > row_limit)) x = -INFINITY;
-        }
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m, mx * c);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    float psum = 0.f;
+    if (__ballot(m_new > m)) {  // some row's max grew: rescale (exact no-op elsewhere)
+      const float alpha = exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    m = m_new;
+    const float neg_m = -m_use;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[kb][r] - m_use);
+        const float p = exp2f(__builtin_fmaf(s[kb][r], c, neg_m));
         s[kb][r] = p;
-        psum += p;
+        l += p;
       }
-    psum += __shfl_xor(psum, 32);
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
 
     // P^T fragments: accumulator entries 8st..8st+7 of key block kb are the
     // keys kb*32 + 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's row.
@@ -180,24 +177,25 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
                                       s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
       }
 
-    // ---- O^T += V^T P^T: V fragment rows = the same key order as P.
-    const int grp = lane >> 4, li = lane & 15;
+    // ---- O^T += V^T P^T: V fragment rows in the same key order as P.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int col = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+      const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);  // logical chunk
+      const int e = 4 * (li & 1);
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int r0 = kb * 32 + 16 * st + 4 * hf + (li >> 2);
-          const s16x4 lo = lds_read_tr(&sm.v[r0 * P + col]);
-          const s16x4 hi = lds_read_tr(&sm.v[(r0 + 8) * P + col]);
+          const s16x4 lo = lds_read_tr(&vs_[lds_off<D>(r0, cl, e)]);
+          const s16x4 hi = lds_read_tr(&vs_[lds_off<D>(r0 + 8, cl, e)]);
           acc[db] = mfma32(concat_bf16(lo, hi), pf[kb * 2 + st], acc[db]);
         }
     }
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
+  l = pair_sum(l);
   if (row_ok) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* orow = a.o + obase + (int64_t)i * a.o_st + (int64_t)h * a.o_sh;
@@ -234,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     if (n_items == 0) continue;
     for (;;) {
       if (threadIdx.x == 0) s_item = atomicAdd(&w.counters[qq], 1);
-      __syncthreads();
+      __syncthreads();  // also: every wave is done with the previous item's LDS
       const int j = s_item;
       __syncthreads();
       if (j >= n_items) break;

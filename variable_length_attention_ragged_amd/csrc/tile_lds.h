@@ -1,0 +1,90 @@
+// Tiles of one head staged in LDS with buffer loads that write LDS directly.
+//
+// A tile is `ROWS` rows x D bf16 of one head of a ragged tensor, stored
+// row-major in LDS in 16-byte chunks, chunk c of row r at chunk position
+// c ^ swz(r).  The XOR keeps both access patterns of the attention kernels
+// free of bank conflicts: 16 consecutive rows at one chunk (MFMA operands
+// read along the head dim) and 4 consecutive rows x 4 consecutive chunks
+// (transposed reads with ds_read_b64_tr_b16).  Rows at or past the tile's
+// valid row count lie outside the buffer resource's range: the hardware
+// returns zeros for them, so pad rows are never read.
+#pragma once
+
+#include "common.h"
+#include "mfma_util.h"
+
+namespace vattn {
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);  // 256-byte rows span all 64 banks
+  } else {
+    const int x = (r >> 1) & 7;             // 128-byte rows: two rows per bank sweep
+    return ((x & 1) << 2) | ((x >> 2) << 1) | ((x >> 1) & 1);
+  }
+}
+
+// Element offset of (row, logical 16-byte chunk c) + `e` elements inside it.
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int c, int e = 0) {
+  return row * D + ((c ^ swz<D>(row)) << 3) + e;
+}
+
+// Buffer resource over rows [0, rows) of one head: base points at row 0,
+// `st` is the row stride in elements, `row_elems` the elements read per row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows,
+                                                           int64_t st, int row_elems,
+                                                           int elem_bytes) {
+  const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * st + row_elems) * elem_bytes) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Enqueue the loads of a ROWS x D tile (rows [0, nrows) valid) into `dst`.
+// Must be called by all 256 threads; completion is tracked by vmcnt.
+template <int D, int ROWS>
+__device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
+                                           uint16_t* dst) {
+  constexpr int CPR = D / 8;
+  constexpr int CH = ROWS * CPR / 256;
+  static_assert(CH >= 1 && ROWS * CPR % 256 == 0, "tile must cover whole waves");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(head_row0, nrows, st, D, 2);
+#pragma unroll
+  for (int n = 0; n < CH; ++n) {
+    const int base_c = (n * 4 + wave) * 64;  // first chunk position this wave writes
+    const int p = base_c + lane;
+    const int r = p / CPR, cl = (p % CPR) ^ swz<D>(r);
+    const int off = (int)(((int64_t)r * st + cl * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)&dst[base_c * 8], 16, off, 0, 0, 0);
+  }
+}
+
+// Enqueue 64 fp32 values (rows [0, nrows) valid, stride `st` elements) into
+// dst[0..63]; called by one whole wave.
+__device__ __forceinline__ void issue_column(const float* row0, int nrows, int64_t st,
+                                             float* dst) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(row0, nrows, st, 1, 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4,
+                                           (int)((int64_t)lane * st * 4), 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_tile_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Swap with the lane 32 apart: returns {own, partner} in some order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                   false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                   false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+}  // namespace vattn
