@@ -205,15 +205,25 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
       }
       const uint16_t* qt = sm.q[buf];
       const uint16_t* dt = sm.dout[buf];
+      {
+        // Q / dO fragments of step ks+1 are read while step ks multiplies.
+        bf16x8 qa[2], da[2];
+        qa[0] = as_bf16x8(load16(&qt[lds_off<D>(l32, hf)]));
+        da[0] = as_bf16x8(load16(&dt[lds_off<D>(l32, hf)]));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(as_bf16x8(load16(&qt[lds_off<D>(l32, 2 * ks + hf)])), kf[ks], s);
-        dp = mfma32(as_bf16x8(load16(&dt[lds_off<D>(l32, 2 * ks + hf)])), vf[ks], dp);
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+            qa[(ks + 1) & 1] = as_bf16x8(load16(&qt[lds_off<D>(l32, 2 * (ks + 1) + hf)]));
+            da[(ks + 1) & 1] = as_bf16x8(load16(&dt[lds_off<D>(l32, 2 * (ks + 1) + hf)]));
+          }
+          s = mfma32(qa[ks & 1], kf[ks], s);
+          dp = mfma32(da[ks & 1], vf[ks], dp);
+        }
       }
       // ---- P and dS (lane: key my_key; entries: query rows)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(s[r] * c);
+        float p = fast_exp2(s[r] * c);
         if (need_mask) {
           const int q = qs + 8 * (r >> 2) + 4 * hf + (r & 3);
           bool ok = q < lq && my_key < lk;
@@ -234,20 +244,27 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
         dsf[st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4], dp[o + 5],
                               dp[o + 6], dp[o + 7]);
       }
-      // ---- dV += P^T dO, dK += dS^T Q (B operands read transposed from LDS)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);
+      // ---- dV += P^T dO, dK += dS^T Q (B operands read transposed from
+      //      LDS one (st, db) step ahead; 2*DB independent accumulator chains)
+      {
         const int e = 4 * (li & 1);
+        const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1);
+        auto read_b = [&](int n, bf16x8& dob, bf16x8& qb) {
+          const int st = n / DB, db = n % DB;
+          const int r0 = 16 * st + 4 * hf + (li >> 2), cl = db * 4 + cl0;
+          dob = concat_bf16(lds_read_tr(&dt[lds_off<D>(r0, cl, e)]),
+                            lds_read_tr(&dt[lds_off<D>(r0 + 8, cl, e)]));
+          qb = concat_bf16(lds_read_tr(&qt[lds_off<D>(r0, cl, e)]),
+                           lds_read_tr(&qt[lds_off<D>(r0 + 8, cl, e)]));
+        };
+        bf16x8 dob[2], qb[2];
+        read_b(0, dob[0], qb[0]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = 16 * st + 4 * hf + (li >> 2);
-          const bf16x8 dob = concat_bf16(lds_read_tr(&dt[lds_off<D>(r0, cl, e)]),
-                                         lds_read_tr(&dt[lds_off<D>(r0 + 8, cl, e)]));
-          const bf16x8 qb = concat_bf16(lds_read_tr(&qt[lds_off<D>(r0, cl, e)]),
-                                        lds_read_tr(&qt[lds_off<D>(r0 + 8, cl, e)]));
-          dv[db] = mfma32(pf[st], dob, dv[db]);
-          dk[db] = mfma32(dsf[st], qb, dk[db]);
+        for (int n = 0; n < 2 * DB; ++n) {
+          if (n + 1 < 2 * DB) read_b(n + 1, dob[(n + 1) & 1], qb[(n + 1) & 1]);
+          const int st = n / DB, db = n % DB;
+          dv[db] = mfma32(pf[st], dob[n & 1], dv[db]);
+          dk[db] = mfma32(dsf[st], qb[n & 1], dk[db]);
         }
       }
     }
@@ -400,14 +417,23 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
         dp[r] = -dl;
       }
       const int row = kb * 32 + l32;
+      {
+        bf16x8 ka[2], va[2];
+        ka[0] = as_bf16x8(load16(&kt[lds_off<D>(row, hf)]));
+        va[0] = as_bf16x8(load16(&vt[lds_off<D>(row, hf)]));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(as_bf16x8(load16(&kt[lds_off<D>(row, 2 * ks + hf)])), qf[ks], s);
-        dp = mfma32(as_bf16x8(load16(&vt[lds_off<D>(row, 2 * ks + hf)])), df[ks], dp);
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+            ka[(ks + 1) & 1] = as_bf16x8(load16(&kt[lds_off<D>(row, 2 * (ks + 1) + hf)]));
+            va[(ks + 1) & 1] = as_bf16x8(load16(&vt[lds_off<D>(row, 2 * (ks + 1) + hf)]));
+          }
+          s = mfma32(ka[ks & 1], qf[ks], s);
+          dp = mfma32(va[ks & 1], df[ks], dp);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(s[r] * c);
+        float p = fast_exp2(s[r] * c);
         if (need_mask) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           const bool ok = key < lk && !(causal && (int64_t)key > row_limit);
@@ -422,20 +448,26 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
                                        dp[o + 5], dp[o + 6], dp[o + 7]);
       }
     }
-    // ---- dQ^T += K^T dS^T: K read transposed, keys in the order of dS^T
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);
+    // ---- dQ^T += K^T dS^T: K read transposed (keys in the order of dS^T)
+    //      one 16-key step ahead; DB independent accumulator chains.
+    {
       const int e = 4 * (li & 1);
+      const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1);
+      auto read_k = [&](int kst, bf16x8* out) {
+        const int r0 = (kst >> 1) * 32 + 16 * (kst & 1) + 4 * hf + (li >> 2);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+        for (int db = 0; db < DB; ++db)
+          out[db] = concat_bf16(lds_read_tr(&kt[lds_off<D>(r0, db * 4 + cl0, e)]),
+                                lds_read_tr(&kt[lds_off<D>(r0 + 8, db * 4 + cl0, e)]));
+      };
+      bf16x8 kfr[2][DB];
+      read_k(0, kfr[0]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = kb * 32 + 16 * st + 4 * hf + (li >> 2);
-          const s16x4 lo = lds_read_tr(&kt[lds_off<D>(r0, cl, e)]);
-          const s16x4 hi = lds_read_tr(&kt[lds_off<D>(r0 + 8, cl, e)]);
-          acc[db] = mfma32(concat_bf16(lo, hi), dsf[kb * 2 + st], acc[db]);
-        }
+      for (int kst = 0; kst < BN / 16; ++kst) {
+        if (kst + 1 < BN / 16) read_k(kst + 1, kfr[(kst + 1) & 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(kfr[kst & 1][db], dsf[kst], acc[db]);
+      }
     }
   }
 

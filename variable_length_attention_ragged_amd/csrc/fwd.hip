@@ -16,11 +16,14 @@
 //   S^T = K Q^T      MFMA 32x32x16 bf16, Q fragments in registers; a lane
 //                    owns one query row, so the row max needs one swap between
 //                    lane halves and the row sum none until the end;
-//   online softmax   max on raw scores, exp2(fma(s, scale*log2e, -m)),
-//                    accumulators rescaled only when some row's max grew;
+//   online softmax   max on raw scores, exp2(fma(s, scale*log2e, -m)); the
+//                    running max is raised (and the accumulators rescaled)
+//                    only when a row's tile max passes it by more than 8;
 //   O^T += V^T P^T   MFMA, V read transposed from LDS (ds_read_b64_tr_b16),
 //                    P taken straight from the S^T accumulators.
 // Query rows past Lq load zeros and are never stored.
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_util.h"
 #include "tile_lds.h"
@@ -41,6 +44,7 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-wide blocks of head_dim
+  constexpr float kRescale = 8.f;  // log2 headroom before the running max is raised
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
@@ -66,7 +70,14 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
   const int i = wq0 + l32;
   const bool row_ok = i < lq;
-  const int64_t row_limit = (int64_t)i + dg;  // last visible key of a causal row
+  // Last visible key of this lane's row and of the wave's first row (keys
+  // past it are masked), clamped to [-1, lk - 1].
+  auto last_key = [&](int64_t row) -> int {
+    if (!causal) return lk - 1;
+    return (int)min(max(row + dg, (int64_t)-1), (int64_t)lk - 1);
+  };
+  const int lim = last_key(i);
+  const int wave_lim = last_key(wq0);
 
   // A negative scale is folded into Q (exact sign flip) so that the row max
   // can be taken on raw scores and c > 0.
@@ -86,6 +97,24 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     }
   }
 
+  // Lane-constant LDS offsets (elements).  The swizzle depends on the row
+  // modulo 16 only, and every step below moves by whole multiples of 16
+  // rows, so each read is one of these registers plus an immediate.
+  //   K (A operand of S^T): row kb*32 + l32, chunk 2ks + hf.
+  //   V (transposed): rows 16-step + rl (lo) and + rl + 8 (hi), chunk
+  //   db*4 + cl0, element e within the chunk.
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = lds_off<D>(l32, 2 * ks + hf);
+  const int rl = 4 * hf + (li >> 2);
+  const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1), e = 4 * (li & 1);
+  int vlo[DB], vhi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    vlo[db] = lds_off<D>(rl, db * 4 + cl0, e);
+    vhi[db] = lds_off<D>(rl + 8, db * 4 + cl0, e);
+  }
+
   // One tile of K and V (rows k0..k0+BN-1 of kv head g) into buffer `buf`.
   const uint16_t* khead = a.k + kbase + (int64_t)g * a.k_sh;
   const uint16_t* vhead = a.v + vbase + (int64_t)g * a.v_sh;
@@ -96,102 +125,122 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
     issue_tile<D, BN>(vhead + (int64_t)k0 * a.v_st, nrows, a.v_st, sm.v[buf]);
   };
 
-  float m = -INFINITY, l = 0.f;  // l: this lane's half of the row sum
+  float m = -INFINITY, l = 0.f;  // m: running max (log2 units, may lag by < 8); l: lane's half sum
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  if (n_kv > 0) load_kv(0, 0);
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
+  // One K/V tile; BUF is a compile-time buffer index so that every LDS
+  // address is a lane register plus an immediate.
+  auto step = [&](auto BUF, int j) {
+    constexpr int buf = decltype(BUF)::value;
     wait_tile_loads();  // this wave's part of tile j landed
     __syncthreads();    // all parts of tile j visible; tile j-1 fully consumed
     if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
     const int k0 = j * BN;
-    if (!wave_active || k0 >= wave_kv_end) continue;
-    const uint16_t* ks_ = sm.k[buf];
-    const uint16_t* vs_ = sm.v[buf];
+    if (!wave_active || k0 >= wave_kv_end) return;
+    const uint16_t* kt = sm.k[buf];
+    const uint16_t* vt = sm.v[buf];
 
-    // ---- S^T = K Q^T  (BN keys x 32 queries per wave)
+    // ---- S^T = K Q^T (BN keys x 32 queries); the two 32-key chains
+    //      alternate and step ks+1's K fragments are read during step ks.
     f32x16 s[BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = kb * 32 + l32;
+    {
+      bf16x8 kfr[2][BN / 32];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[kb] = mfma32(as_bf16x8(load16(&ks_[lds_off<D>(row, 2 * ks + hf)])), qf[ks], s[kb]);
+      for (int kb = 0; kb < BN / 32; ++kb)
+        kfr[0][kb] = as_bf16x8(load16(kt + koff[0] + kb * 32 * D));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb)
+            kfr[(ks + 1) & 1][kb] = as_bf16x8(load16(kt + koff[ks + 1] + kb * 32 * D));
+        }
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) s[kb] = mfma32(kfr[ks & 1][kb], qf[ks], s[kb]);
+      }
     }
 
-    // ---- mask (boundary tiles only), row max on raw scores
-    const bool need_mask =
-        (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
-    if (need_mask) {
+    // ---- mask (boundary tiles only): entry (kb, r) is key
+    //      k0 + kb*32 + 8(r/4) + 4hf + r%4, masked when past `lim`.
+    if (k0 + BN - 1 > wave_lim) {
+      const int th = lim - k0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= lk || (causal && (int64_t)key > row_limit)) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > th) s[kb][r] = -INFINITY;
     }
+
+    // ---- online softmax on raw scores (c > 0)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    if (__ballot(m_new > m)) {  // some row's max grew: rescale (exact no-op elsewhere)
-      const float alpha = exp2f(m - m_use);
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    mx = pair_max(mx) * c;
+    // Raise the running max only when some row's tile max exceeds it by more
+    // than kRescale: weights stay below 2^8, and the rescale (one multiply
+    // per accumulator) runs on few tiles.  Exact either way: O and l share m.
+    if (__ballot(mx > m + kRescale)) {
+      const float m_new = fmaxf(m, mx);
+      // rows with no visible key yet keep m = -inf (l and acc are 0 there)
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m = m_new;
     }
-    m = m_new;
-    const float neg_m = -m_use;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(__builtin_fmaf(s[kb][r], c, neg_m));
-        s[kb][r] = p;
-        l += p;
-      }
-
-    // P^T fragments: accumulator entries 8st..8st+7 of key block kb are the
-    // keys kb*32 + 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's row.
+    const float neg_m = (m == -INFINITY) ? 0.f : -m;
     bf16x8 pf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int o = 8 * st;
-        pf[kb * 2 + st] = pack_bf16x8(s[kb][o], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
-                                      s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
+        float p[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          p[x] = fast_exp2(__builtin_fmaf(s[kb][8 * st + x], c, neg_m));
+          l += p[x];
+        }
+        // entries 8st..8st+7 of block kb are keys
+        // kb*32 + 16st + {4hf..4hf+3, 8+4hf..8+4hf+3}
+        pf[kb * 2 + st] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       }
 
-    // ---- O^T += V^T P^T: V fragment rows in the same key order as P.
+    // ---- O^T += V^T P^T: V read transposed in P's key order, one 16-key
+    //      step ahead; DB independent accumulator chains.
+    {
+      bf16x8 vfr[2][DB];
+      auto read_v = [&](int kst, bf16x8* out) {
+        const int base = ((kst >> 1) * 32 + 16 * (kst & 1)) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int cl = db * 4 + 2 * (grp & 1) + ((li & 3) >> 1);  // logical chunk
-      const int e = 4 * (li & 1);
+        for (int db = 0; db < DB; ++db)
+          out[db] = concat_bf16(lds_read_tr(vt + vlo[db] + base), lds_read_tr(vt + vhi[db] + base));
+      };
+      read_v(0, vfr[0]);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kst = 0; kst < BN / 16; ++kst) {
+        if (kst + 1 < BN / 16) read_v(kst + 1, vfr[(kst + 1) & 1]);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = kb * 32 + 16 * st + 4 * hf + (li >> 2);
-          const s16x4 lo = lds_read_tr(&vs_[lds_off<D>(r0, cl, e)]);
-          const s16x4 hi = lds_read_tr(&vs_[lds_off<D>(r0 + 8, cl, e)]);
-          acc[db] = mfma32(concat_bf16(lo, hi), pf[kb * 2 + st], acc[db]);
-        }
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32(vfr[kst & 1][db], pf[kst], acc[db]);
+      }
     }
+  };
+
+  if (n_kv > 0) load_kv(0, 0);
+  for (int j = 0; j < n_kv; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_kv) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2

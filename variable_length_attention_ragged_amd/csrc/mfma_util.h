@@ -43,11 +43,13 @@ __device__ inline bf16x8 concat_bf16(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ inline uint16_t to_bf16_bits(float a) {
@@ -71,6 +73,10 @@ __device__ inline int xcc_id() {
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(r));
   return (int)(r & 0xf);
 }
+
+// 2^x with the hardware's v_exp_f32 (no denormal rescaling: results below
+// 2^-126 flush to zero, which is harmless for softmax weights).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline u32x4 load16(const uint16_t* p) { return *(const u32x4*)p; }
 __device__ inline void store16(uint16_t* p, u32x4 v) { *(u32x4*)p = v; }
