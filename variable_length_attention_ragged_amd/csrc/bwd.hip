@@ -22,6 +22,8 @@
 // dQ is accumulated in registers by a query-major pass instead of fp32
 // atomics from the key-major pass: that recomputes S and dP once more (14*D
 // flops per pair instead of 10*D) but writes every dQ element once.
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_util.h"
 #include "tile_lds.h"
@@ -169,106 +171,147 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
     if (wave == 1) issue_column(w.delta + loff, nrows, a.lse_st, sm.delta[buf]);
   };
 
+  // Lane-constant LDS offsets into a Q or dO tile (elements); query block qb
+  // (rows 32qb..32qb+31) and 16-row steps add immediates:
+  //   natural (A operand of S and dP): row l32, chunk 2ks + hf;
+  //   transposed (B operand of dV and dK): rows rl (lo) and rl + 8 (hi).
+  int qoff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qoff[ks] = lds_off<D>(l32, 2 * ks + hf);
+  const int rl = 4 * hf + (li >> 2);
+  const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1), e = 4 * (li & 1);
+  int tlo[DB], thi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    tlo[db] = lds_off<D>(rl, db * 4 + cl0, e);
+    thi[db] = lds_off<D>(rl + 8, db * 4 + cl0, e);
+  }
+  constexpr int QB = BM / 32;  // 32-row query blocks per tile
+
+  // The work of one query tile from LDS buffer BUF; MASKED selects the
+  // boundary-tile variant.  Each variant is one branch-free block, so the
+  // MFMAs of one query block can overlap the exp/dS arithmetic of the other.
+  auto compute = [&](auto BUF, auto MASKED, int qs, int lq, int lk, bool causal, int64_t dg) {
+    constexpr int buf = decltype(BUF)::value;
+    constexpr bool masked = decltype(MASKED)::value;
+    const uint16_t* qt = sm.q[buf];
+    const uint16_t* dt = sm.dout[buf];
+
+    // ---- S = Q K^T and dP = dO V^T per query block.  Accumulators start
+    //      at -LSE*log2(e)/c and -delta, so s*c = S*scale*log2(e) -
+    //      LSE*log2(e) and dp = dP - delta.  Entry r of block qb is query row
+    //      32qb + 8(r/4) + 4hf + r%4.
+    f32x16 s[QB], dp[QB];
+    {
+      const float inv_c = 1.f / c;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const f32x4 x = *(const f32x4*)&sm.lse[buf][32 * qb + 8 * rr + 4 * hf];
+          const f32x4 y = *(const f32x4*)&sm.delta[buf][32 * qb + 8 * rr + 4 * hf];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s[qb][4 * rr + q] = -x[q] * kLog2e * inv_c;
+            dp[qb][4 * rr + q] = -y[q];
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 qa[QB], da[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          qa[qb] = as_bf16x8(load16(qt + qoff[ks] + qb * 32 * D));
+          da[qb] = as_bf16x8(load16(dt + qoff[ks] + qb * 32 * D));
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb] = mfma32(qa[qb], kf[ks], s[qb]);
+          dp[qb] = mfma32(da[qb], vf[ks], dp[qb]);
+        }
+      }
+    }
+    // ---- P and dS (lane: key my_key).  Boundary tiles keep entry (qb, r)
+    //      when lo <= 32qb + 8(r/4) + r%4 < hi.
+    int lo = -1, hi = BM;
+    if constexpr (masked) {
+      const int base = qs + 4 * hf;
+      lo = causal ? (int)min(max((int64_t)my_key - dg - base, (int64_t)-1), (int64_t)BM) : -1;
+      hi = my_key < lk ? min(lq - base, BM) : -1;
+    }
+    bf16x8 pf[QB][2], dsf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(s[qb][r] * c);
+        if constexpr (masked) {
+          const int q = 32 * qb + 8 * (r >> 2) + (r & 3);
+          p = (q >= lo && q < hi) ? p : 0.f;
+        }
+        s[qb][r] = p;
+        dp[qb][r] = p * dp[qb][r];
+      }
+      // entries 8st..8st+7 are query rows 32qb + 16st + {4hf..+3, 8+4hf..+3}
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        pf[qb][st] = pack_bf16x8(s[qb][o], s[qb][o + 1], s[qb][o + 2], s[qb][o + 3],
+                                 s[qb][o + 4], s[qb][o + 5], s[qb][o + 6], s[qb][o + 7]);
+        dsf[qb][st] = pack_bf16x8(dp[qb][o], dp[qb][o + 1], dp[qb][o + 2], dp[qb][o + 3],
+                                  dp[qb][o + 4], dp[qb][o + 5], dp[qb][o + 6], dp[qb][o + 7]);
+      }
+    }
+    // ---- dV += P^T dO, dK += dS^T Q: B operands read transposed one
+    //      (16-row step, db) ahead; 2*DB independent accumulator chains.
+    {
+      constexpr int NSTEP = 2 * QB * DB;
+      auto read_b = [&](int n, bf16x8& dob, bf16x8& qbf) {
+        const int kst = n / DB, db = n % DB;  // kst: 16-row step = 2*qb + st
+        const int off = 16 * kst * D;
+        dob = concat_bf16(lds_read_tr(dt + tlo[db] + off), lds_read_tr(dt + thi[db] + off));
+        qbf = concat_bf16(lds_read_tr(qt + tlo[db] + off), lds_read_tr(qt + thi[db] + off));
+      };
+      bf16x8 dob[2], qbf[2];
+      read_b(0, dob[0], qbf[0]);
+#pragma unroll
+      for (int n = 0; n < NSTEP; ++n) {
+        if (n + 1 < NSTEP) read_b(n + 1, dob[(n + 1) & 1], qbf[(n + 1) & 1]);
+        const int kst = n / DB, db = n % DB;
+        dv[db] = mfma32(pf[kst >> 1][kst & 1], dob[n & 1], dv[db]);
+        dk[db] = mfma32(dsf[kst >> 1][kst & 1], qbf[n & 1], dk[db]);
+      }
+    }
+  };
+
+  // One query tile; BUF is the compile-time LDS buffer of `cur`.
   QPos cur = seek(QPos{0, 0, 0, false});
-  if (!cur.done) issue(cur, 0);
-  for (int n = 0; !cur.done; ++n) {
-    const int buf = n & 1;
+  auto step = [&](auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
     const QPos nx = next(cur);
     wait_tile_loads();
-    __syncthreads();  // tile n visible to all waves; tile n-1 fully consumed
+    __syncthreads();  // this tile visible to all waves; the previous one consumed
     if (!nx.done) issue(nx, buf ^ 1);
-
     const int b = bfirst + cur.mi;
     const int lq = w.lq[b], lk = w.lk[b];
     const bool causal = w.policy[b] != VARLEN_ATTN_PADDING;
     const int64_t dg = w.diag[b];
     const int qs = cur.qs;
-    const bool skip = wk0 >= lk || (causal && (int64_t)wk0 > (int64_t)(qs + BM - 1) + dg);
-    if (!skip) {
-      const bool need_mask = qs + BM > lq || wk0 + 32 > lk ||
-                             (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
-      // ---- S = Q K^T and dP = dO V^T (32 queries x this wave's 32 keys).
-      // The accumulators start at the per-row terms, -LSE*log2(e)/c and
-      // -delta, so that afterwards s*c = S*scale*log2(e) - LSE*log2(e) and
-      // dp = dP - delta.  Entry r is query row 8*(r/4) + 4hf + r%4.
-      f32x16 s, dp;
-      const float inv_c = 1.f / c;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const f32x4 x = *(const f32x4*)&sm.lse[buf][8 * rr + 4 * hf];
-        const f32x4 y = *(const f32x4*)&sm.delta[buf][8 * rr + 4 * hf];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[4 * rr + e] = -x[e] * kLog2e * inv_c;
-          dp[4 * rr + e] = -y[e];
-        }
-      }
-      const uint16_t* qt = sm.q[buf];
-      const uint16_t* dt = sm.dout[buf];
-      {
-        // Q / dO fragments of step ks+1 are read while step ks multiplies.
-        bf16x8 qa[2], da[2];
-        qa[0] = as_bf16x8(load16(&qt[lds_off<D>(l32, hf)]));
-        da[0] = as_bf16x8(load16(&dt[lds_off<D>(l32, hf)]));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS) {
-            qa[(ks + 1) & 1] = as_bf16x8(load16(&qt[lds_off<D>(l32, 2 * (ks + 1) + hf)]));
-            da[(ks + 1) & 1] = as_bf16x8(load16(&dt[lds_off<D>(l32, 2 * (ks + 1) + hf)]));
-          }
-          s = mfma32(qa[ks & 1], kf[ks], s);
-          dp = mfma32(da[ks & 1], vf[ks], dp);
-        }
-      }
-      // ---- P and dS (lane: key my_key; entries: query rows)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * c);
-        if (need_mask) {
-          const int q = qs + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool ok = q < lq && my_key < lk;
-          if (causal) ok = ok && (int64_t)my_key <= (int64_t)q + dg;
-          p = ok ? p : 0.f;
-        }
-        s[r] = p;
-        dp[r] = p * dp[r];
-      }
-      // P^T / dS^T fragments: entries 8st..8st+7 are query rows
-      // 16st + {4hf..4hf+3, 8+4hf..8+4hf+3} of this lane's key.
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int o = 8 * st;
-        pf[st] = pack_bf16x8(s[o], s[o + 1], s[o + 2], s[o + 3], s[o + 4], s[o + 5], s[o + 6],
-                             s[o + 7]);
-        dsf[st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4], dp[o + 5],
-                              dp[o + 6], dp[o + 7]);
-      }
-      // ---- dV += P^T dO, dK += dS^T Q (B operands read transposed from
-      //      LDS one (st, db) step ahead; 2*DB independent accumulator chains)
-      {
-        const int e = 4 * (li & 1);
-        const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1);
-        auto read_b = [&](int n, bf16x8& dob, bf16x8& qb) {
-          const int st = n / DB, db = n % DB;
-          const int r0 = 16 * st + 4 * hf + (li >> 2), cl = db * 4 + cl0;
-          dob = concat_bf16(lds_read_tr(&dt[lds_off<D>(r0, cl, e)]),
-                            lds_read_tr(&dt[lds_off<D>(r0 + 8, cl, e)]));
-          qb = concat_bf16(lds_read_tr(&qt[lds_off<D>(r0, cl, e)]),
-                           lds_read_tr(&qt[lds_off<D>(r0 + 8, cl, e)]));
-        };
-        bf16x8 dob[2], qb[2];
-        read_b(0, dob[0], qb[0]);
-#pragma unroll
-        for (int n = 0; n < 2 * DB; ++n) {
-          if (n + 1 < 2 * DB) read_b(n + 1, dob[(n + 1) & 1], qb[(n + 1) & 1]);
-          const int st = n / DB, db = n % DB;
-          dv[db] = mfma32(pf[st], dob[n & 1], dv[db]);
-          dk[db] = mfma32(dsf[st], qb[n & 1], dk[db]);
-        }
-      }
-    }
     cur = nx;
+    if (wk0 >= lk || (causal && (int64_t)wk0 > (int64_t)(qs + BM - 1) + dg)) return;
+    const bool masked = qs + BM > lq || wk0 + 32 > lk ||
+                        (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
+    if (masked)
+      compute(BUF, std::true_type{}, qs, lq, lk, causal, dg);
+    else
+      compute(BUF, std::false_type{}, qs, lq, lk, causal, dg);
+  };
+
+  if (!cur.done) issue(cur, 0);
+  while (!cur.done) {
+    step(std::integral_constant<int, 0>{});
+    if (cur.done) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // ---- dK * scale, dV as bf16 for key rows < lmax.  acc[r] holds
@@ -347,7 +390,13 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
     wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
   const int i = wq0 + l32;
   const bool row_ok = i < lq;
-  const int64_t row_limit = (int64_t)i + dg;
+  // Last visible key of this lane's row and of the wave's first row.
+  auto last_key = [&](int64_t row) -> int {
+    if (!causal) return lk - 1;
+    return (int)min(max(row + dg, (int64_t)-1), (int64_t)lk - 1);
+  };
+  const int lim = last_key(i);
+  const int wave_lim = last_key(wq0);
 
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -384,61 +433,69 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
     issue_tile<D, BN>(vhead + (int64_t)k0 * a.v_st, nrows, a.v_st, sm.v[buf]);
   };
 
+  // Lane-constant LDS offsets (see the forward): natural reads of K and V
+  // (row kb*32 + l32, chunk 2ks + hf) and transposed reads of K.
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = lds_off<D>(l32, 2 * ks + hf);
+  const int rl = 4 * hf + (li >> 2);
+  const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1), e = 4 * (li & 1);
+  int klo[DB], khi[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    klo[db] = lds_off<D>(rl, db * 4 + cl0, e);
+    khi[db] = lds_off<D>(rl + 8, db * 4 + cl0, e);
+  }
+
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  if (n_kv > 0) load_kv(0, 0);
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
+  auto step = [&](auto BUF, int j) {
+    constexpr int buf = decltype(BUF)::value;
     wait_tile_loads();
     __syncthreads();
     if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
     const int k0 = j * BN;
-    if (!wave_active || k0 >= wave_kv_end) continue;
+    if (!wave_active || k0 >= wave_kv_end) return;
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
+    const bool masked = k0 + BN - 1 > wave_lim;
+    const int th = lim - k0 - 4 * hf;  // entry (kb, r) masked when its key offset > th
 
     // ---- per 32-key block: S^T = K Q^T and dP^T = V dO^T, then
     //      dS^T = P^T o (dP^T - delta).  The accumulators start at the row
-    //      terms (-LSE*log2(e)/c and -delta) so no separate subtraction is
-    //      needed.  Lane: query row i; entry r: key 8*(r/4) + 4hf + r%4.
-    const bool need_mask =
-        (k0 + BN > lk) || (causal && (int64_t)(k0 + BN - 1) > (int64_t)wq0 + dg);
+    //      terms (-LSE*log2(e)/c and -delta).  Lane: query row i; entry r:
+    //      key kb*32 + 8(r/4) + 4hf + r%4.
     bf16x8 dsf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
-      f32x16 s, dp;
+      f32x16 sc, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = s_init;
+        sc[r] = s_init;
         dp[r] = -dl;
       }
-      const int row = kb * 32 + l32;
       {
         bf16x8 ka[2], va[2];
-        ka[0] = as_bf16x8(load16(&kt[lds_off<D>(row, hf)]));
-        va[0] = as_bf16x8(load16(&vt[lds_off<D>(row, hf)]));
+        ka[0] = as_bf16x8(load16(kt + koff[0] + kb * 32 * D));
+        va[0] = as_bf16x8(load16(vt + koff[0] + kb * 32 * D));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + 1 < KS) {
-            ka[(ks + 1) & 1] = as_bf16x8(load16(&kt[lds_off<D>(row, 2 * (ks + 1) + hf)]));
-            va[(ks + 1) & 1] = as_bf16x8(load16(&vt[lds_off<D>(row, 2 * (ks + 1) + hf)]));
+            ka[(ks + 1) & 1] = as_bf16x8(load16(kt + koff[ks + 1] + kb * 32 * D));
+            va[(ks + 1) & 1] = as_bf16x8(load16(vt + koff[ks + 1] + kb * 32 * D));
           }
-          s = mfma32(ka[ks & 1], qf[ks], s);
+          sc = mfma32(ka[ks & 1], qf[ks], sc);
           dp = mfma32(va[ks & 1], df[ks], dp);
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * c);
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool ok = key < lk && !(causal && (int64_t)key > row_limit);
-          p = ok ? p : 0.f;
-        }
+        float p = fast_exp2(sc[r] * c);
+        if (masked && kb * 32 + 8 * (r >> 2) + (r & 3) > th) p = 0.f;
         dp[r] = p * dp[r];
       }
 #pragma unroll
@@ -448,27 +505,24 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
                                        dp[o + 5], dp[o + 6], dp[o + 7]);
       }
     }
-    // ---- dQ^T += K^T dS^T: K read transposed (keys in the order of dS^T)
-    //      one 16-key step ahead; DB independent accumulator chains.
-    {
-      const int e = 4 * (li & 1);
-      const int cl0 = 2 * (grp & 1) + ((li & 3) >> 1);
-      auto read_k = [&](int kst, bf16x8* out) {
-        const int r0 = (kst >> 1) * 32 + 16 * (kst & 1) + 4 * hf + (li >> 2);
+    // ---- dQ^T += K^T dS^T: K read transposed (keys in the order of dS^T);
+    //      DB independent accumulator chains per 16-key step.
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          out[db] = concat_bf16(lds_read_tr(&kt[lds_off<D>(r0, db * 4 + cl0, e)]),
-                                lds_read_tr(&kt[lds_off<D>(r0 + 8, db * 4 + cl0, e)]));
-      };
-      bf16x8 kfr[2][DB];
-      read_k(0, kfr[0]);
+    for (int kst = 0; kst < BN / 16; ++kst) {
+      const int base = ((kst >> 1) * 32 + 16 * (kst & 1)) * D;
+      bf16x8 kfr[DB];
 #pragma unroll
-      for (int kst = 0; kst < BN / 16; ++kst) {
-        if (kst + 1 < BN / 16) read_k(kst + 1, kfr[(kst + 1) & 1]);
+      for (int db = 0; db < DB; ++db)
+        kfr[db] = concat_bf16(lds_read_tr(kt + klo[db] + base), lds_read_tr(kt + khi[db] + base));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32(kfr[kst & 1][db], dsf[kst], acc[db]);
-      }
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32(kfr[db], dsf[kst], acc[db]);
     }
+  };
+
+  if (n_kv > 0) load_kv(0, 0);
+  for (int j = 0; j < n_kv; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_kv) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (row_ok) {
@@ -487,7 +541,7 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
   __shared__ int s_item;
   const WsView& w = a.ws;

@@ -9,11 +9,11 @@
 namespace vattn {
 
 // Tile sizes.  Forward and dQ pass: 4 waves x 32 query rows, 64-key K/V
-// tiles.  dK/dV pass: 4 waves x 32 key rows stay resident while 32-row query
+// tiles.  dK/dV pass: 4 waves x 32 key rows stay resident while 64-row query
 // tiles stream past.
 constexpr int kFwdBlockM = 128;
 constexpr int kFwdBlockN = 64;
-constexpr int kBwdBlockM = 32;
+constexpr int kBwdBlockM = 64;
 constexpr int kBwdBlockN = 128;
 constexpr int kQueues = 8;        // one claim queue per XCD (8 XCDs on MI355X)
 constexpr float kLog2eHost = 1.4426950408889634f;
