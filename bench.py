@@ -60,6 +60,34 @@ def fwd_bytes(batch) -> int:
             + q_rows * batch.h_q * 4)
 
 
+def kernel_fingerprint() -> str:
+    """sha256 over the HIP sources, as recorded next to the profiled traffic."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "variable_length_attention_ragged_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str):
+    """Calibrated HBM bytes per launch of `kernel` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload, or None when
+    the kernel sources have changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic__packed_causal_h32_d128.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_fingerprint") != kernel_fingerprint():
+        return None
+    entry = rec.get("per_launch", {}).get(kernel)
+    return None if entry is None else entry["total_bytes"]
+
+
 def cpu_baseline(batch, target_s: float = 15.0):
     """Time the fp64 oracle's forward, as it stands, on a bounded sample of the
     same workload: every sequence for the first n query heads, n chosen from a
@@ -221,7 +249,7 @@ def main(argv=None) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(dominant),
         },
         "cpu_baseline": None,
     }
