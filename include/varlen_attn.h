@@ -149,8 +149,11 @@ typedef struct varlen_attn_problem {
  *             tile of bwd_block_n key rows of a group of consecutive
  *             sequences that bind the same K, V, dK and dV rows
  *   scratch   setup kernel scratch
- *   delta     fp32 rowsum(dO * O), same element offsets as LSE (backward
- *             only) */
+ *   delta     fp32 -rowsum(dO * O), same element offsets as LSE (backward
+ *             only)
+ *   lse_term  fp32 -LSE * log2(e) / max(|scale * log2(e)|, 1e-30), same
+ *             element offsets as LSE (backward only): the row term that
+ *             the backward kernels start their score accumulators from */
 typedef struct varlen_attn_layout {
   int64_t total_bytes;
   int64_t counters_offset;
@@ -164,6 +167,7 @@ typedef struct varlen_attn_layout {
   int64_t scratch_offset;
   int64_t delta_offset;
   int64_t delta_elems;
+  int64_t lse_term_offset;
   int32_t fwd_block_m;
   int32_t fwd_block_n;
   int32_t bwd_block_m;
@@ -179,8 +183,8 @@ typedef struct varlen_attn_layout {
 int varlen_attn_fwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* o,
                                      varlen_attn_layout* out);
 
-/* Workspace layout of a backward call.  delta mirrors lse element for
- * element, so it is sized from the caller's span of lse, which counts every
+/* Workspace layout of a backward call.  delta and lse_term mirror lse
+ * element for element, so it is sized from the caller's span of lse, which counts every
  * axis (cudnn-frontend PR #462, "The fix (commit 1)": size from every stride
  * axis; a head-major [h, t] LSE needs h*t elements, not t).  Host only. */
 int varlen_attn_bwd_workspace_layout(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
@@ -246,7 +250,8 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
  * exactly: varlen_attn_fwd = fwd_setup, fwd_attention;
  * varlen_attn_bwd = bwd_setup, bwd_preprocess, bwd_dkdv, bwd_dq.
  *   fwd_attention    O and LSE of every listed tile
- *   bwd_preprocess   delta = rowsum(dO * O) (fp32, in the workspace)
+ *   bwd_preprocess   -delta = -rowsum(dO * O) and lse_term (fp32, in the
+ *                    workspace)
  *   bwd_dkdv         dK and dV (bf16), key-major: K/V resident, query tiles
  *                    streamed
  *   bwd_dq           dQ (bf16), query-major: Q/dO resident, K/V tiles

@@ -140,7 +140,8 @@ def test_token_major_workspace_identities(T, h, d):
     L = _bwd_layout(lse, dq, dk, _p(batch=3, h_q=h, h_kv=h, d=d))
     assert L.delta_elems == T * h                 # softmax_sum = maxT * h_q
     assert L.total_bytes >= L.delta_offset + 4 * T * h
-    assert L.delta_offset % 256 == 0
+    assert L.total_bytes >= L.lse_term_offset + 4 * T * h
+    assert L.delta_offset % 256 == 0 and L.lse_term_offset % 256 == 0
 
 
 def test_regions_are_disjoint_and_ordered():
@@ -152,7 +153,8 @@ def test_regions_are_disjoint_and_ordered():
                (L.seq_offset, L.seq_i64_offset + 72 * 37),
                (L.fwd_tiles_offset, 8 * L.fwd_tiles_capacity),
                (L.bwd_tiles_offset, 16 * L.bwd_tiles_capacity),
-               (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems)]
+               (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems),
+               (L.lse_term_offset, 4 * L.delta_elems)]
     for (a, n), (b, _) in zip(regions, regions[1:]):
         assert a + n <= b and b % 256 == 0
     assert regions[-1][0] + regions[-1][1] <= L.total_bytes

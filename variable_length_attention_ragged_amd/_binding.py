@@ -40,7 +40,7 @@ class varlen_attn_layout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in (
         "total_bytes", "counters_offset", "header_offset", "seq_offset", "seq_i64_offset",
         "fwd_tiles_offset", "fwd_tiles_capacity", "bwd_tiles_offset", "bwd_tiles_capacity",
-        "scratch_offset", "delta_offset", "delta_elems")] + \
+        "scratch_offset", "delta_offset", "delta_elems", "lse_term_offset")] + \
         [(n, c_int32) for n in ("fwd_block_m", "fwd_block_n", "bwd_block_m", "bwd_block_n")]
 
 

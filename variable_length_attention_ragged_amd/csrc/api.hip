@@ -104,6 +104,7 @@ void base_layout(int64_t B, int64_t fwd_cap, int64_t bwd_cap, varlen_attn_layout
   L->scratch_offset = off;
   off += align256(64 * B);
   L->delta_offset = off;
+  L->lse_term_offset = off;
   L->total_bytes = off;
   L->fwd_block_m = kFwdBlockM;
   L->fwd_block_n = kFwdBlockN;
@@ -126,6 +127,7 @@ WsView make_view(char* ws, const varlen_attn_layout& L, int64_t B) {
   w.bwd_tiles = (int32_t*)(ws + L.bwd_tiles_offset);
   w.scratch = ws + L.scratch_offset;
   w.delta = (float*)(ws + L.delta_offset);
+  w.lse_term = (float*)(ws + L.lse_term_offset);
   w.fwd_cap = L.fwd_tiles_capacity;
   w.bwd_cap = L.bwd_tiles_capacity;
   return w;
@@ -171,6 +173,8 @@ int bwd_layout(const varlen_attn_problem* p, const varlen_attn_tensor* lse,
   int64_t off = L->total_bytes;
   L->delta_offset = off;
   L->delta_elems = lse->span_elems;
+  off += align256(lse->span_elems * 4);
+  L->lse_term_offset = off;
   off += align256(lse->span_elems * 4);
   L->total_bytes = off;
   return VARLEN_ATTN_OK;

@@ -1,7 +1,8 @@
 // Backward kernels: preprocess, dK/dV pass, dQ pass.
 //
-//   preprocess   delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32).  delta lives
-//                in the workspace with the element offsets of LSE, as the
+//   preprocess   delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32), stored
+//                negated, and the score row term -LSE[i,h]*log2(e)/c.  Both
+//                live in the workspace with the element offsets of LSE, as the
 //                softmax row-sum intermediate of cudnn-frontend PR #462 ("Root
 //                cause") lives on its user tensor's strides, which is why the
 //                workspace is sized from LSE's full span.
@@ -41,15 +42,16 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
   constexpr int RPP = 64 / LPR;        // rows per wave pass
   const WsView& w = a.ws;
   const int B = a.batch;
-  const int n_items = w.header[0] * a.h_q;
+  const int n_items = ldm(w.header + 0) * a.h_q;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane % LPR, lr = lane / LPR;
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int tile = item / a.h_q, h = item - tile * a.h_q;
-    const int b = w.fwd_tiles[2 * tile], t = w.fwd_tiles[2 * tile + 1];
-    const int lq = w.lq[b];
-    const int64_t obase = w.base[T_O * B + b], dobase = w.base[T_DO * B + b];
-    const int64_t lbase = w.base[T_LSE * B + b];
+    const int b = ldm(w.fwd_tiles + (2 * tile)), t = ldm(w.fwd_tiles + (2 * tile + 1));
+    const int lq = ldm(w.lq + b);
+    const int64_t obase = ldm(w.base + (T_O * B + b)), dobase = ldm(w.base + (T_DO * B + b));
+    const int64_t lbase = ldm(w.base + (T_LSE * B + b));
     const int r_end = min(kFwdBlockM, lq - t * kFwdBlockM);
     for (int r = wave * RPP + lr; r < r_end; r += 4 * RPP) {
       const int64_t i = (int64_t)t * kFwdBlockM + r;
@@ -61,19 +63,26 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (li == 0) w.delta[lbase + i * a.lse_st + (int64_t)h * a.lse_sh] = acc;
+      if (li == 0) {
+        const int64_t off = lbase + i * a.lse_st + (int64_t)h * a.lse_sh;
+        w.delta[off] = -acc;
+        w.lse_term[off] = -a.lse[off] * kLog2e / c;
+      }
     }
   }
 }
 
 // ------------------------------------------------------------ dK / dV
 
+// Double-buffered query tiles.  Each buffer is its own LDS variable: the
+// compiler then tells apart reads of one buffer from the in-flight LDS-DMA
+// writes into the other and waits for those only where they overlap.
 template <int D>
 struct DkdvSmem {
-  uint16_t q[2][kBwdBlockM * D];
-  uint16_t dout[2][kBwdBlockM * D];
-  float lse[2][64];
-  float delta[2][64];
+  uint16_t* q[2];     // kBwdBlockM x D
+  uint16_t* dout[2];  // kBwdBlockM x D
+  float* lt[2];       // score row term -LSE*log2(e)/c; -inf past the tile's rows
+  float* nd[2];       // -delta
 };
 
 struct QPos {
@@ -82,20 +91,23 @@ struct QPos {
 };
 
 template <int D>
-__device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entry, int g) {
+__device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t* entry, int g) {
   constexpr int BM = kBwdBlockM, BN = kBwdBlockN;
   constexpr int KS = D / 16, DB = D / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int QB = BM / 32;  // 32-row query blocks per tile
+  static_assert(BM == 64, "one lane per tile row in the row-term fixup");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
   const WsView& w = a.ws;
 
-  const int bfirst = entry[0], members = entry[1], u = entry[2], lmax = entry[3];
+  const int bfirst = ldm(entry + 0), members = ldm(entry + 1), u = ldm(entry + 2), lmax = ldm(entry + 3);
   const int k0 = u * BN;
   const int wk0 = k0 + wave * 32;
   const int my_key = wk0 + l32;
-  const int64_t kbase = w.base[T_K * B + bfirst], vbase = w.base[T_V * B + bfirst];
-  const int64_t dkbase = w.base[T_DK * B + bfirst], dvbase = w.base[T_DV * B + bfirst];
+  const int64_t kbase = ldm(w.base + (T_K * B + bfirst)), vbase = ldm(w.base + (T_V * B + bfirst));
+  const int64_t dkbase = ldm(w.base + (T_DK * B + bfirst)), dvbase = ldm(w.base + (T_DV * B + bfirst));
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
@@ -122,14 +134,14 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
     }
 
   // Query tiles to visit, in order: query heads of the group, member
-  // sequences, 32-row tiles from the first row that can see key k0.
+  // sequences, BM-row tiles from the first row that can see key k0.
   auto first_row = [&](int mi, int& lo) -> bool {
     const int b = bfirst + mi;
-    const int lq = w.lq[b], lk = w.lk[b];
+    const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
     if (lq <= 0 || lk <= k0) return false;
     lo = 0;
-    if (w.policy[b] != VARLEN_ATTN_PADDING) {
-      const int64_t first = (int64_t)k0 - w.diag[b];
+    if (ldm(w.policy + b) != VARLEN_ATTN_PADDING) {
+      const int64_t first = (int64_t)k0 - ldm(w.diag + b);
       if (first >= lq) return false;
       lo = (int)max(first, (int64_t)0);
       lo -= lo % BM;
@@ -154,21 +166,21 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
   };
   auto next = [&](QPos p) -> QPos {
     p.qs += BM;
-    if (p.qs < w.lq[bfirst + p.mi]) return p;
+    if (p.qs < ldm(w.lq + (bfirst + p.mi))) return p;
     ++p.mi;
     return seek(p);
   };
   auto issue = [&](const QPos& p, int buf) {
     const int b = bfirst + p.mi, h = g * a.group + p.hh;
-    const int nrows = min(BM, w.lq[b] - p.qs);
+    const int nrows = min(BM, ldm(w.lq + b) - p.qs);
     const int64_t qs = p.qs;
-    issue_tile<D, BM>(a.q + w.base[T_Q * B + b] + qs * a.q_st + (int64_t)h * a.q_sh, nrows, a.q_st,
+    issue_tile<D, BM>(a.q + ldm(w.base + (T_Q * B + b)) + qs * a.q_st + (int64_t)h * a.q_sh, nrows, a.q_st,
                       sm.q[buf]);
-    issue_tile<D, BM>(a.dout + w.base[T_DO * B + b] + qs * a.do_st + (int64_t)h * a.do_sh, nrows,
+    issue_tile<D, BM>(a.dout + ldm(w.base + (T_DO * B + b)) + qs * a.do_st + (int64_t)h * a.do_sh, nrows,
                       a.do_st, sm.dout[buf]);
-    const int64_t loff = w.base[T_LSE * B + b] + qs * a.lse_st + (int64_t)h * a.lse_sh;
-    if (wave == 0) issue_column(a.lse + loff, nrows, a.lse_st, sm.lse[buf]);
-    if (wave == 1) issue_column(w.delta + loff, nrows, a.lse_st, sm.delta[buf]);
+    const int64_t loff = ldm(w.base + (T_LSE * B + b)) + qs * a.lse_st + (int64_t)h * a.lse_sh;
+    if (wave == 0) issue_column(w.lse_term + loff, nrows, a.lse_st, sm.lt[buf]);
+    if (wave == 1) issue_column(w.delta + loff, nrows, a.lse_st, sm.nd[buf]);
   };
 
   // Lane-constant LDS offsets into a Q or dO tile (elements); query block qb
@@ -186,101 +198,122 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
     tlo[db] = lds_off<D>(rl, db * 4 + cl0, e);
     thi[db] = lds_off<D>(rl + 8, db * 4 + cl0, e);
   }
-  constexpr int QB = BM / 32;  // 32-row query blocks per tile
+  const int rto = 4 * hf;  // row-term offset: entries 4r'..4r'+3 are rows 8r' + 4hf + 0..3
 
-  // The work of one query tile from LDS buffer BUF; MASKED selects the
-  // boundary-tile variant.  Each variant is one branch-free block, so the
-  // MFMAs of one query block can overlap the exp/dS arithmetic of the other.
-  auto compute = [&](auto BUF, auto MASKED, int qs, int lq, int lk, bool causal, int64_t dg) {
+  // The work of one query tile from LDS buffer BUF.  Entry r of query block
+  // qb is tile row 32qb + 8(r/4) + 4hf + r%4 against key my_key.  The S
+  // accumulators start at the row term (so s*c = S*scale*log2(e) -
+  // LSE*log2(e)) and dP's at -delta.  Masked pairs start at -inf, which
+  // makes P and dS exactly zero: rows past the tile's end through the LDS
+  // row term, keys past lk and above the causal diagonal through `th` (keep
+  // entry r iff 32qb + 8(r/4) + r%4 >= th), applied only when `masked`.
+  //
+  // The tile runs as four phases of 16 MFMAs each, software-pipelined by
+  // hand (scheduling barriers keep the order): LDS operands are read two
+  // steps ahead, and the exp/dS arithmetic of one query block runs in the
+  // shadow of the other block's MFMAs:
+  //   A  S, dP of block 0          B  S, dP of block 1   + P, dS of block 0
+  //   C  dV, dK from block 0       D  dV, dK from block 1 (+ P, dS of block 1
+  //                                   finishing in C)
+  auto compute = [&](auto BUF, bool masked, int th) {
     constexpr int buf = decltype(BUF)::value;
-    constexpr bool masked = decltype(MASKED)::value;
     const uint16_t* qt = sm.q[buf];
     const uint16_t* dt = sm.dout[buf];
 
-    // ---- S = Q K^T and dP = dO V^T per query block.  Accumulators start
-    //      at -LSE*log2(e)/c and -delta, so s*c = S*scale*log2(e) -
-    //      LSE*log2(e) and dp = dP - delta.  Entry r of block qb is query row
-    //      32qb + 8(r/4) + 4hf + r%4.
     f32x16 s[QB], dp[QB];
-    {
-      const float inv_c = 1.f / c;
+    const float* ltp = sm.lt[buf] + rto;
+    const float* ndp = sm.nd[buf] + rto;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x4 x = *(const f32x4*)(ltp + 32 * qb + 8 * rr);
+        const f32x4 y = *(const f32x4*)(ndp + 32 * qb + 8 * rr);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s[qb][4 * rr + q] = x[q];
+          dp[qb][4 * rr + q] = y[q];
+        }
+      }
+    if (masked) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const f32x4 x = *(const f32x4*)&sm.lse[buf][32 * qb + 8 * rr + 4 * hf];
-          const f32x4 y = *(const f32x4*)&sm.delta[buf][32 * qb + 8 * rr + 4 * hf];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            s[qb][4 * rr + q] = -x[q] * kLog2e * inv_c;
-            dp[qb][4 * rr + q] = -y[q];
-          }
-        }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 qa[QB], da[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          qa[qb] = as_bf16x8(load16(qt + qoff[ks] + qb * 32 * D));
-          da[qb] = as_bf16x8(load16(dt + qoff[ks] + qb * 32 * D));
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[qb] = mfma32(qa[qb], kf[ks], s[qb]);
-          dp[qb] = mfma32(da[qb], vf[ks], dp[qb]);
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          s[qb][r] = 32 * qb + 8 * (r >> 2) + (r & 3) >= th ? s[qb][r] : -INFINITY;
     }
-    // ---- P and dS (lane: key my_key).  Boundary tiles keep entry (qb, r)
-    //      when lo <= 32qb + 8(r/4) + r%4 < hi.
-    int lo = -1, hi = BM;
-    if constexpr (masked) {
-      const int base = qs + 4 * hf;
-      lo = causal ? (int)min(max((int64_t)my_key - dg - base, (int64_t)-1), (int64_t)BM) : -1;
-      hi = my_key < lk ? min(lq - base, BM) : -1;
-    }
+
+    // Operand streams.  Natural step i (0..2KS-1): block i/KS, ks = i%KS.
+    // Transposed step n (0..4DB-1): block n/(2DB), 16-row half st =
+    // (n/DB)%2, db = n%DB.
+    constexpr int NN = QB * KS, NT = QB * 2 * DB;
+    static_assert(QB == 2, "four-phase schedule");
+    bf16x8 na[3], nb[3];  // Q, dO fragments of natural steps, ring of 3
+    bf16x8 ta[3], tb[3];  // dO, Q fragments of transposed steps, ring of 3
+    auto ld_nat = [&](int i) {
+      const int qb = i / KS, ks = i % KS;
+      na[i % 3] = as_bf16x8(load16(qt + qoff[ks] + qb * 32 * D));
+      nb[i % 3] = as_bf16x8(load16(dt + qoff[ks] + qb * 32 * D));
+    };
+    auto ld_tr = [&](int n) {
+      const int kst = n / DB, db = n % DB;  // kst: 16-row step = 2*qb + st
+      const int off = 16 * kst * D;
+      ta[n % 3] = concat_bf16(lds_read_tr(dt + tlo[db] + off), lds_read_tr(dt + thi[db] + off));
+      tb[n % 3] = concat_bf16(lds_read_tr(qt + tlo[db] + off), lds_read_tr(qt + thi[db] + off));
+    };
+    // Load for global step g of the combined stream (natural, then transposed).
+    auto ld = [&](int g) {
+      if (g < NN) ld_nat(g);
+      else if (g < NN + NT) ld_tr(g - NN);
+    };
+
     bf16x8 pf[QB][2], dsf[QB][2];
+    float pe[QB][8], de[QB][8];
+    // P and dS of entries 2k, 2k+1 of block qb; packs after every 4th chunk.
+    auto softmax2 = [&](int qb, int k) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[qb][r] * c);
-        if constexpr (masked) {
-          const int q = 32 * qb + 8 * (r >> 2) + (r & 3);
-          p = (q >= lo && q < hi) ? p : 0.f;
-        }
-        s[qb][r] = p;
-        dp[qb][r] = p * dp[qb][r];
+      for (int j = 0; j < 2; ++j) {
+        const int r = 2 * k + j;
+        const float p = fast_exp2(s[qb][r] * c);
+        pe[qb][r & 7] = p;
+        de[qb][r & 7] = p * dp[qb][r];
       }
-      // entries 8st..8st+7 are query rows 32qb + 16st + {4hf..+3, 8+4hf..+3}
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int o = 8 * st;
-        pf[qb][st] = pack_bf16x8(s[qb][o], s[qb][o + 1], s[qb][o + 2], s[qb][o + 3],
-                                 s[qb][o + 4], s[qb][o + 5], s[qb][o + 6], s[qb][o + 7]);
-        dsf[qb][st] = pack_bf16x8(dp[qb][o], dp[qb][o + 1], dp[qb][o + 2], dp[qb][o + 3],
-                                  dp[qb][o + 4], dp[qb][o + 5], dp[qb][o + 6], dp[qb][o + 7]);
+      if ((k & 3) == 3) {
+        const int st = k >> 2;
+        pf[qb][st] = pack_bf16x8(pe[qb][0], pe[qb][1], pe[qb][2], pe[qb][3], pe[qb][4],
+                                 pe[qb][5], pe[qb][6], pe[qb][7]);
+        dsf[qb][st] = pack_bf16x8(de[qb][0], de[qb][1], de[qb][2], de[qb][3], de[qb][4],
+                                  de[qb][5], de[qb][6], de[qb][7]);
       }
+    };
+
+    ld(0);
+    ld(1);
+    // A, B: S and dP.
+#pragma unroll
+    for (int i = 0; i < NN; ++i) {
+      ld(i + 2);
+      const int qb = i / KS, ks = i % KS;
+      s[qb] = mfma32(na[i % 3], kf[ks], s[qb]);
+      dp[qb] = mfma32(nb[i % 3], vf[ks], dp[qb]);
+      if (qb == 1) {
+#pragma unroll
+        for (int k = 0; k < 8 / KS; ++k) softmax2(0, ks * (8 / KS) + k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- dV += P^T dO, dK += dS^T Q: B operands read transposed one
-    //      (16-row step, db) ahead; 2*DB independent accumulator chains.
-    {
-      constexpr int NSTEP = 2 * QB * DB;
-      auto read_b = [&](int n, bf16x8& dob, bf16x8& qbf) {
-        const int kst = n / DB, db = n % DB;  // kst: 16-row step = 2*qb + st
-        const int off = 16 * kst * D;
-        dob = concat_bf16(lds_read_tr(dt + tlo[db] + off), lds_read_tr(dt + thi[db] + off));
-        qbf = concat_bf16(lds_read_tr(qt + tlo[db] + off), lds_read_tr(qt + thi[db] + off));
-      };
-      bf16x8 dob[2], qbf[2];
-      read_b(0, dob[0], qbf[0]);
+    // C, D: dV += P^T dO, dK += dS^T Q.
 #pragma unroll
-      for (int n = 0; n < NSTEP; ++n) {
-        if (n + 1 < NSTEP) read_b(n + 1, dob[(n + 1) & 1], qbf[(n + 1) & 1]);
-        const int kst = n / DB, db = n % DB;
-        dv[db] = mfma32(pf[kst >> 1][kst & 1], dob[n & 1], dv[db]);
-        dk[db] = mfma32(dsf[kst >> 1][kst & 1], qbf[n & 1], dk[db]);
+    for (int n = 0; n < NT; ++n) {
+      ld(NN + n + 2);
+      const int kst = n / DB, db = n % DB;
+      dv[db] = mfma32(pf[kst >> 1][kst & 1], ta[n % 3], dv[db]);
+      dk[db] = mfma32(dsf[kst >> 1][kst & 1], tb[n % 3], dk[db]);
+      if (n < 2 * DB) {
+#pragma unroll
+        for (int k = 0; k < 4 / DB; ++k) softmax2(1, n * (4 / DB) + k);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -289,22 +322,25 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
   auto step = [&](auto BUF) {
     constexpr int buf = decltype(BUF)::value;
     const QPos nx = next(cur);
+    const int b = bfirst + cur.mi;
+    const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
+    const int qs = cur.qs;
     wait_tile_loads();
+    // Rows past the sequence's end: the row term loaded as 0, make it -inf.
+    if (wave == 0 && qs + lane >= lq) sm.lt[buf][lane] = -INFINITY;
     __syncthreads();  // this tile visible to all waves; the previous one consumed
     if (!nx.done) issue(nx, buf ^ 1);
-    const int b = bfirst + cur.mi;
-    const int lq = w.lq[b], lk = w.lk[b];
-    const bool causal = w.policy[b] != VARLEN_ATTN_PADDING;
-    const int64_t dg = w.diag[b];
-    const int qs = cur.qs;
+    const bool causal = ldm(w.policy + b) != VARLEN_ATTN_PADDING;
+    const int64_t dg = ldm(w.diag + b);
     cur = nx;
     if (wk0 >= lk || (causal && (int64_t)wk0 > (int64_t)(qs + BM - 1) + dg)) return;
-    const bool masked = qs + BM > lq || wk0 + 32 > lk ||
-                        (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
-    if (masked)
-      compute(BUF, std::true_type{}, qs, lq, lk, causal, dg);
-    else
-      compute(BUF, std::false_type{}, qs, lq, lk, causal, dg);
+    const bool masked = wk0 + 32 > lk || (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
+    int th = -1;
+    if (my_key >= lk)
+      th = BM;
+    else if (causal)
+      th = (int)min(max((int64_t)my_key - dg - qs, (int64_t)-1), (int64_t)BM);
+    compute(BUF, masked, th - 4 * hf);
   };
 
   if (!cur.done) issue(cur, 0);
@@ -332,10 +368,14 @@ __device__ void dkdv_item(const BwdArgs& a, DkdvSmem<D>& sm, const int32_t* entr
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) uint16_t q0[kBwdBlockM * D], q1[kBwdBlockM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t d0[kBwdBlockM * D], d1[kBwdBlockM * D];
+  __shared__ __attribute__((aligned(16))) float lt0[kBwdBlockM], lt1[kBwdBlockM];
+  __shared__ __attribute__((aligned(16))) float nd0[kBwdBlockM], nd1[kBwdBlockM];
   __shared__ int s_item;
+  DkdvSmem<D> sm{{q0, q1}, {d0, d1}, {lt0, lt1}, {nd0, nd1}};
   const WsView& w = a.ws;
-  const int n_tiles = w.header[1];
+  const int n_tiles = ldm(w.header + 1);
   const int xcd = xcc_id() & (kQueues - 1);
   for (int qi = 0; qi < kQueues; ++qi) {
     const int qq = (xcd + qi) & (kQueues - 1);
@@ -356,14 +396,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ dQ
 
+// Double-buffered K and V tiles, one LDS variable per buffer (as above).
 template <int D>
 struct DqSmem {
-  uint16_t k[2][kFwdBlockN * D];
-  uint16_t v[2][kFwdBlockN * D];
+  uint16_t* k[2];
+  uint16_t* v[2];
 };
 
 template <int D>
-__device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, int g) {
+__device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int h, int g) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -371,12 +412,12 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
   const int B = a.batch;
   const WsView& w = a.ws;
 
-  const int lq = w.lq[b], lk = w.lk[b];
-  const int64_t dg = w.diag[b];
-  const bool causal = w.policy[b] != VARLEN_ATTN_PADDING;
-  const int64_t qbase = w.base[T_Q * B + b], dobase = w.base[T_DO * B + b];
-  const int64_t kbase = w.base[T_K * B + b], vbase = w.base[T_V * B + b];
-  const int64_t lbase = w.base[T_LSE * B + b], dqbase = w.base[T_DQ * B + b];
+  const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
+  const int64_t dg = ldm(w.diag + b);
+  const bool causal = ldm(w.policy + b) != VARLEN_ATTN_PADDING;
+  const int64_t qbase = ldm(w.base + (T_Q * B + b)), dobase = ldm(w.base + (T_DO * B + b));
+  const int64_t kbase = ldm(w.base + (T_K * B + b)), vbase = ldm(w.base + (T_V * B + b));
+  const int64_t lbase = ldm(w.base + (T_LSE * B + b)), dqbase = ldm(w.base + (T_DQ * B + b));
 
   const int q0 = t * BM;
   const int rows = min(BM, lq - q0);
@@ -419,7 +460,7 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
     }
     if (row_ok) {
       const int64_t off = lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh;
-      s_init = -a.lse[off] * kLog2e / c;
+      s_init = w.lse_term[off];
       dl = w.delta[off];
     }
   }
@@ -476,7 +517,7 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sc[r] = s_init;
-        dp[r] = -dl;
+        dp[r] = dl;
       }
       {
         bf16x8 ka[2], va[2];
@@ -542,10 +583,12 @@ __device__ void dq_tile(const BwdArgs& a, DqSmem<D>& sm, int b, int t, int h, in
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
   __shared__ int s_item;
+  DqSmem<D> sm{{k0, k1}, {v0, v1}};
   const WsView& w = a.ws;
-  const int n_tiles = w.header[0];
+  const int n_tiles = ldm(w.header + 0);
   const int xcd = xcc_id() & (kQueues - 1);
   const int group = a.group;
   const int per_g = n_tiles * group;
@@ -563,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       const int gi = j / per_g, rem = j - gi * per_g;
       const int tile = rem / group, hh = rem - tile * group;
       const int g = qq + kQueues * gi;
-      dq_tile<D>(a, sm, w.fwd_tiles[2 * tile], w.fwd_tiles[2 * tile + 1], g * group + hh, g);
+      dq_tile<D>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
     }
   }
 }

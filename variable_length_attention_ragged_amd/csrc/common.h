@@ -37,6 +37,16 @@ struct DevTensor {
   int32_t present;
 };
 
+// Workspace metadata (sequence table, tile lists, header) is written by the
+// setup kernel before any compute launch and only read afterwards.  Reading
+// it through the constant address space lets uniform reads become scalar
+// loads: they neither wait for nor hold up the vector-memory tile loads, and
+// buffer descriptors built from them stay in scalar registers.
+template <class T>
+__device__ __forceinline__ T ldm(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Pointers into one workspace, following varlen_attn_layout.
 struct WsView {
   int32_t* counters;
@@ -50,7 +60,8 @@ struct WsView {
   int32_t* fwd_tiles;   // (b, t) pairs
   int32_t* bwd_tiles;   // (first, members, u, max_lk) quadruples
   char* scratch;
-  float* delta;
+  float* delta;       // -rowsum(dO * O) at LSE's element offsets
+  float* lse_term;    // -LSE * log2(e) / c at LSE's element offsets
   int64_t fwd_cap;
   int64_t bwd_cap;
 };

@@ -33,14 +33,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The double-buffered K and V tiles.  Each buffer is its own LDS variable:
+// the compiler then tells apart reads of one buffer from the in-flight
+// LDS-DMA writes into the other and waits for those only where they overlap.
 template <int D>
 struct FwdSmem {
-  uint16_t k[2][kFwdBlockN * D];
-  uint16_t v[2][kFwdBlockN * D];
+  uint16_t* k[2];
+  uint16_t* v[2];
 };
 
 template <int D>
-__device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, int g) {
+__device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, int h, int g) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-wide blocks of head_dim
@@ -50,12 +53,12 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
   const int B = a.batch;
   const WsView& w = a.ws;
 
-  const int lq = w.lq[b], lk = w.lk[b], pol = w.policy[b];
-  const int64_t dg = w.diag[b];
+  const int lq = ldm(w.lq + b), lk = ldm(w.lk + b), pol = ldm(w.policy + b);
+  const int64_t dg = ldm(w.diag + b);
   const bool causal = pol != VARLEN_ATTN_PADDING;
-  const int64_t qbase = w.base[T_Q * B + b], kbase = w.base[T_K * B + b];
-  const int64_t vbase = w.base[T_V * B + b], obase = w.base[T_O * B + b];
-  const int64_t lbase = w.base[T_LSE * B + b];
+  const int64_t qbase = ldm(w.base + (T_Q * B + b)), kbase = ldm(w.base + (T_K * B + b));
+  const int64_t vbase = ldm(w.base + (T_V * B + b)), obase = ldm(w.base + (T_O * B + b));
+  const int64_t lbase = ldm(w.base + (T_LSE * B + b));
 
   const int q0 = t * BM;
   const int rows = min(BM, lq - q0);
@@ -267,10 +270,12 @@ __device__ void fwd_tile(const FwdArgs& a, FwdSmem<D>& sm, int b, int t, int h, 
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
   __shared__ int s_item;
+  FwdSmem<D> sm{{k0, k1}, {v0, v1}};
   const WsView& w = a.ws;
-  const int n_tiles = w.header[0];
+  const int n_tiles = ldm(w.header + 0);
   const int xcd = xcc_id() & (kQueues - 1);
   const int group = a.group;
   const int per_g = n_tiles * group;
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       const int gi = j / per_g, rem = j - gi * per_g;
       const int tile = rem / group, hh = rem - tile * group;
       const int g = qq + kQueues * gi;
-      fwd_tile<D>(a, sm, w.fwd_tiles[2 * tile], w.fwd_tiles[2 * tile + 1], g * group + hh, g);
+      fwd_tile<D>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
     }
   }
 }

@@ -32,10 +32,11 @@ __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, 
 // row i); result lane i' receives M[4j + i'/4][i'%4] for j = 0..3.  Pointing
 // source lane i at row (r0 + i/4), column (c0 + 4*(i%4)) of a row-major tile
 // therefore hands lane i' the 4 rows r0..r0+3 of column c0 + i'.
+// `p` must point into LDS; the address-space cast keeps constant offsets
+// foldable into the instruction's offset field.
 __device__ inline s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)(
-          (uintptr_t)p)));
+      (__attribute__((address_space(3))) s16x4*)(p));
 }
 
 __device__ inline bf16x8 concat_bf16(s16x4 lo, s16x4 hi) {

@@ -40,22 +40,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
+// v + s, computed where it stands: the asm keeps the compiler from hoisting
+// the per-load offsets below out of the tile loop, where each would hold a
+// register for the whole kernel.
+__device__ __forceinline__ int add_in_place(int v, int s) {
+  int r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
+  return r;
+}
+
 // Enqueue the loads of a ROWS x D tile (rows [0, nrows) valid) into `dst`.
 // Must be called by all 256 threads; completion is tracked by vmcnt.
+// Load n of a lane covers row r0 + n*RSTEP at the same chunk position as
+// row r0 (the swizzle repeats every 16 rows), so its offset is the lane's
+// first offset plus a uniform step.
 template <int D, int ROWS>
 __device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
                                            uint16_t* dst) {
   constexpr int CPR = D / 8;
   constexpr int CH = ROWS * CPR / 256;
+  constexpr int RSTEP = 256 / CPR;
   static_assert(CH >= 1 && ROWS * CPR % 256 == 0, "tile must cover whole waves");
+  static_assert(RSTEP % 16 == 0, "swizzle period must divide the row step");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc(head_row0, nrows, st, D, 2);
+  const int p = wave * 64 + lane;
+  const int r0 = p / CPR, cl = (p % CPR) ^ swz<D>(r0);
+  const int voff = (int)(((int64_t)r0 * st + cl * 8) * 2);
+  const int step = (int)((int64_t)RSTEP * st * 2);
 #pragma unroll
   for (int n = 0; n < CH; ++n) {
     const int base_c = (n * 4 + wave) * 64;  // first chunk position this wave writes
-    const int p = base_c + lane;
-    const int r = p / CPR, cl = (p % CPR) ^ swz<D>(r);
-    const int off = (int)(((int64_t)r * st + cl * 8) * 2);
+    const int off = n == 0 ? voff : add_in_place(voff, n * step);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)&dst[base_c * 8], 16, off, 0, 0, 0);
   }
