@@ -82,7 +82,13 @@ SETUP_CASES = [
     ("cfg5_small", lambda: workloads.config5(doc_len=4096, chunk=512, offsets=(512, 3584))),
 ] + [(f"random{s}", (lambda s=s: workloads.random_batch(s, batch=9, max_len=300,
                                                          q_causal_offset=bool(s % 2))))
-     for s in range(100, 106)]
+     for s in range(100, 106)] + [
+    # more sequences (and kv groups) than the setup kernel ranks from LDS, and
+    # tile lists longer than one block-scan chunk
+    ("random_b1100", lambda: workloads.random_batch(300, batch=1100, max_len=12, max_gap=4)),
+    ("random_b2200", lambda: workloads.random_batch(301, batch=2200, max_len=6, max_gap=2,
+                                                    cross=False)),
+]
 
 
 @pytest.mark.parametrize("name,make", SETUP_CASES, ids=[c[0] for c in SETUP_CASES])
@@ -115,6 +121,20 @@ def test_random_fwd_bwd(seed, dim):
     batch = workloads.random_batch(seed, batch=6, max_len=300, h_q=4, h_kv=2, dim=dim,
                                    q_causal_offset=(seed % 3 == 0))
     say(f"[random] seed={seed} D={dim} lq={batch.lq.tolist()} lk={batch.lk.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+def test_many_tiny_sequences_fwd_bwd():
+    """1100 sequences of 0..12 rows: almost every tile is a ragged tail, and the
+    setup ranks more sequences than it keeps in LDS."""
+    batch = workloads.random_batch(302, batch=1100, max_len=12, max_gap=3, h_q=4, h_kv=2,
+                                   dim=128)
+    say(f"[tiny] B={batch.batch} tokens={int(batch.lq.sum())}")
     dev = _dev(batch)
     dev.fwd()
     dev.bwd()

@@ -23,6 +23,9 @@ namespace vattn {
 namespace {
 
 constexpr int kSetupThreads = 1024;
+// Batches up to this size rank their sequences and kv groups from LDS copies
+// of the sort keys; larger ones read them from the workspace scratch.
+constexpr int kLdsSeq = 1024;
 
 __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -37,43 +40,56 @@ __device__ int check_tensor(const DevTensor& t, int64_t base, int64_t rows) {
 }
 
 // Sum over the query tiles of max(1, number of key tiles the tile reaches).
+// Lengths are below 2^31, so the divisions run in 32 bits.
 __device__ int64_t sequence_cost(int64_t lq, int64_t lk, bool causal, int64_t diag, int bm,
                                  int bn) {
   int64_t cost = 0;
-  const int64_t n = ceil_div64(lq, bm);
-  for (int64_t t = 0; t < n; ++t) {
-    const int64_t row_end = min(lq, (t + 1) * bm);
+  const uint32_t n = (uint32_t)((lq + bm - 1) / bm);
+  for (uint32_t t = 0; t < n; ++t) {
+    const int64_t row_end = min(lq, (int64_t)(t + 1) * bm);
     int64_t kv_end = lk;
     if (causal) kv_end = min(max(row_end + diag, (int64_t)0), lk);
-    cost += max((int64_t)1, ceil_div64(kv_end, bn));
+    cost += max(1u, ((uint32_t)kv_end + (uint32_t)bn - 1) / (uint32_t)bn);
   }
   return cost;
 }
 
 // Exclusive block-wide scan of value(i) for i in [0, n) into out[i]; returns
-// the total.  Every thread of the block must call it.
+// the total.  Every thread of the block must call it.  Each wave scans its 64
+// values with shuffles; the 16 wave totals are then scanned by one wave.
 template <class F>
 __device__ int64_t block_exclusive_scan(int n, F value, int32_t* out) {
-  __shared__ int64_t buf[kSetupThreads];
+  constexpr int kWaves = kSetupThreads / 64;
+  __shared__ int64_t wave_sum[kWaves];
   __shared__ int64_t carry;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int c = 0; c < n; c += kSetupThreads) {
     const int i = c + tid;
     const int64_t v = (i < n) ? value(i) : 0;
-    buf[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kSetupThreads; off <<= 1) {
-      const int64_t add = (tid >= off) ? buf[tid - off] : 0;
-      __syncthreads();
-      buf[tid] += add;
-      __syncthreads();
+    int64_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
     }
-    const int64_t incl = buf[tid];
-    if (i < n) out[i] = (int32_t)(carry + incl - v);
+    if (lane == 63) wave_sum[wave] = incl;
     __syncthreads();
-    if (tid == kSetupThreads - 1) carry += incl;
+    if (wave == 0) {
+      int64_t ws = lane < kWaves ? wave_sum[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kWaves; off <<= 1) {
+        const int64_t up = __shfl_up(ws, off);
+        if (lane >= off) ws += up;
+      }
+      if (lane < kWaves) wave_sum[lane] = ws;  // inclusive prefix over waves
+    }
+    __syncthreads();
+    const int64_t before = carry + (wave > 0 ? wave_sum[wave - 1] : 0);
+    if (i < n) out[i] = (int32_t)(before + incl - v);
+    __syncthreads();
+    if (tid == 0) carry += wave_sum[kWaves - 1];
     __syncthreads();
   }
   const int64_t total = carry;
@@ -150,14 +166,28 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   }
   __syncthreads();
 
-  // ---- forward tile list: rank listed sequences by (cost desc, index asc)
+  // ---- forward tile list: rank listed sequences by (cost desc, index asc).
+  //      Sort key: the cost of a listed sequence, -1 for the others.
+  __shared__ int64_t s_key[kLdsSeq];
+  __shared__ int32_t s_first[kLdsSeq];
+  const bool in_lds = B <= kLdsSeq;
   auto listed = [&](int b) { return (w.flags[b] & 1) && w.lq[b] > 0; };
+  if (in_lds)
+    for (int b = tid; b < B; b += kSetupThreads) s_key[b] = listed(b) ? cost_f[b] : -1;
+  __syncthreads();
   for (int b = tid; b < B; b += kSetupThreads) {
     if (!listed(b)) continue;
     const int64_t cb = cost_f[b];
     int r = 0;
-    for (int o = 0; o < B; ++o)
-      if (listed(o) && (cost_f[o] > cb || (cost_f[o] == cb && o < b))) ++r;
+    if (in_lds) {
+      for (int o = 0; o < B; ++o) {
+        const int64_t co = s_key[o];
+        r += (co > cb || (co == cb && o < b)) ? 1 : 0;
+      }
+    } else {
+      for (int o = 0; o < B; ++o)
+        if (listed(o) && (cost_f[o] > cb || (cost_f[o] == cb && o < b))) ++r;
+    }
     order[r] = b;
   }
   __syncthreads();
@@ -201,11 +231,26 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     }
     n_groups = (int)total_starts;
     __syncthreads();
+    const bool g_in_lds = n_groups <= kLdsSeq;
+    if (g_in_lds)
+      for (int g = tid; g < n_groups; g += kSetupThreads) {
+        s_key[g] = gcost[g];
+        s_first[g] = gfirst[g];
+      }
+    __syncthreads();
     for (int g = tid; g < n_groups; g += kSetupThreads) {
       const int64_t cg = gcost[g];
+      const int fg = gfirst[g];
       int r = 0;
-      for (int o = 0; o < n_groups; ++o)
-        if (gcost[o] > cg || (gcost[o] == cg && gfirst[o] < gfirst[g])) ++r;
+      if (g_in_lds) {
+        for (int o = 0; o < n_groups; ++o) {
+          const int64_t co = s_key[o];
+          r += (co > cg || (co == cg && s_first[o] < fg)) ? 1 : 0;
+        }
+      } else {
+        for (int o = 0; o < n_groups; ++o)
+          if (gcost[o] > cg || (gcost[o] == cg && gfirst[o] < fg)) ++r;
+      }
       gorder[r] = g;
     }
     __syncthreads();

@@ -49,32 +49,60 @@ __device__ __forceinline__ int add_in_place(int v, int s) {
   return r;
 }
 
-// Enqueue the loads of a ROWS x D tile (rows [0, nrows) valid) into `dst`.
-// Must be called by all 256 threads; completion is tracked by vmcnt.
-// Load n of a lane covers row r0 + n*RSTEP at the same chunk position as
-// row r0 (the swizzle repeats every 16 rows), so its offset is the lane's
-// first offset plus a uniform step.
+// The loads of a ROWS x D tile (rows [0, nrows) valid) into `dst`, prepared
+// once and issued chunk by chunk (chunk n: rows r0 + n*RSTEP of every lane),
+// so that a kernel can spread them between its own instructions instead of
+// stalling on a full memory queue.  Must be used by all 256 threads;
+// completion is tracked by vmcnt.  Load n of a lane covers row r0 + n*RSTEP
+// at the same chunk position as row r0 (the swizzle repeats every 16 rows),
+// so its offset is the lane's first offset plus a uniform step.  With
+// nrows <= 0 the loads touch no memory and write zeros.
 template <int D, int ROWS>
-__device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
-                                           uint16_t* dst) {
-  constexpr int CPR = D / 8;
-  constexpr int CH = ROWS * CPR / 256;
-  constexpr int RSTEP = 256 / CPR;
+struct TileLoad {
+  static constexpr int CPR = D / 8;
+  static constexpr int CH = ROWS * CPR / 256;
+  static constexpr int RSTEP = 256 / CPR;
   static_assert(CH >= 1 && ROWS * CPR % 256 == 0, "tile must cover whole waves");
   static_assert(RSTEP % 16 == 0, "swizzle period must divide the row step");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(head_row0, nrows, st, D, 2);
-  const int p = wave * 64 + lane;
-  const int r0 = p / CPR, cl = (p % CPR) ^ swz<D>(r0);
-  const int voff = (int)(((int64_t)r0 * st + cl * 8) * 2);
-  const int step = (int)((int64_t)RSTEP * st * 2);
-#pragma unroll
-  for (int n = 0; n < CH; ++n) {
+
+  // Per-lane byte offset of load 0 and the uniform step between loads, for
+  // a row stride of st elements; the same for every tile of one tensor.
+  struct Geom {
+    int voff, step;
+  };
+  static __device__ __forceinline__ Geom geom(int64_t st) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = wave * 64 + lane;
+    const int r0 = p / CPR, cl = (p % CPR) ^ swz<D>(r0);
+    return Geom{(int)(((int64_t)r0 * st + cl * 8) * 2), (int)((int64_t)RSTEP * st * 2)};
+  }
+
+  __amdgpu_buffer_rsrc_t rs;
+  Geom g;
+  uint16_t* dst;
+
+  __device__ __forceinline__ TileLoad(const Geom& g_, const uint16_t* head_row0, int nrows,
+                                      int64_t st, uint16_t* dst_)
+      : rs(rows_rsrc(head_row0, nrows, st, D, 2)), g(g_), dst(dst_) {}
+  __device__ __forceinline__ TileLoad(const uint16_t* head_row0, int nrows, int64_t st,
+                                      uint16_t* dst_)
+      : TileLoad(geom(st), head_row0, nrows, st, dst_) {}
+  __device__ __forceinline__ void issue(int n) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int base_c = (n * 4 + wave) * 64;  // first chunk position this wave writes
-    const int off = n == 0 ? voff : add_in_place(voff, n * step);
+    const int off = n == 0 ? g.voff : add_in_place(g.voff, n * g.step);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)&dst[base_c * 8], 16, off, 0, 0, 0);
   }
+};
+
+// All loads of a tile at once.
+template <int D, int ROWS>
+__device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
+                                           uint16_t* dst) {
+  const TileLoad<D, ROWS> t(head_row0, nrows, st, dst);
+#pragma unroll
+  for (int n = 0; n < TileLoad<D, ROWS>::CH; ++n) t.issue(n);
 }
 
 // Enqueue 64 fp32 values (rows [0, nrows) valid, stride `st` elements) into
