@@ -2,7 +2,11 @@
 
 The library is built in-tree next to this file.  Every HIP source is compiled
 with packed-fp32 instruction selection disabled (the compiler still emits
-scalar fp32) and with hardware fp32 atomics for the dQ accumulation.
+scalar fp32).  The backward source additionally asks for MFMA results in
+ordinary vector registers: the dK/dV kernel otherwise keeps its score
+accumulators in accumulation registers and copies every element out and back
+for the softmax arithmetic (measured 3% slower on the packed causal
+workload).
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libvarlen_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ("api.hip", "setup.hip", "fwd.hip", "bwd.hip")
+EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -27,14 +32,15 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list:
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags() + EXTRA_FLAGS.get(src, []) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")

@@ -56,13 +56,15 @@ __device__ __forceinline__ int add_in_place(int v, int s) {
 // completion is tracked by vmcnt.  Load n of a lane covers row r0 + n*RSTEP
 // at the same chunk position as row r0 (the swizzle repeats every 16 rows),
 // so its offset is the lane's first offset plus a uniform step.  With
-// nrows <= 0 the loads touch no memory and write zeros.
-template <int D, int ROWS>
+// nrows <= 0 the loads touch no memory and write zeros.  NT is the number of
+// threads of the block, all of which take part.
+template <int D, int ROWS, int NT = 256>
 struct TileLoad {
   static constexpr int CPR = D / 8;
-  static constexpr int CH = ROWS * CPR / 256;
-  static constexpr int RSTEP = 256 / CPR;
-  static_assert(CH >= 1 && ROWS * CPR % 256 == 0, "tile must cover whole waves");
+  static constexpr int NW = NT / 64;
+  static constexpr int CH = ROWS * CPR / NT;
+  static constexpr int RSTEP = NT / CPR;
+  static_assert(CH >= 1 && ROWS * CPR % NT == 0, "tile must cover whole waves");
   static_assert(RSTEP % 16 == 0, "swizzle period must divide the row step");
 
   // Per-lane byte offset of load 0 and the uniform step between loads, for
@@ -89,7 +91,7 @@ struct TileLoad {
       : TileLoad(geom(st), head_row0, nrows, st, dst_) {}
   __device__ __forceinline__ void issue(int n) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int base_c = (n * 4 + wave) * 64;  // first chunk position this wave writes
+    const int base_c = (n * NW + wave) * 64;  // first chunk position this wave writes
     const int off = n == 0 ? g.voff : add_in_place(g.voff, n * g.step);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)&dst[base_c * 8], 16, off, 0, 0, 0);
@@ -97,12 +99,12 @@ struct TileLoad {
 };
 
 // All loads of a tile at once.
-template <int D, int ROWS>
+template <int D, int ROWS, int NT = 256>
 __device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
                                            uint16_t* dst) {
-  const TileLoad<D, ROWS> t(head_row0, nrows, st, dst);
+  const TileLoad<D, ROWS, NT> t(head_row0, nrows, st, dst);
 #pragma unroll
-  for (int n = 0; n < TileLoad<D, ROWS>::CH; ++n) t.issue(n);
+  for (int n = 0; n < TileLoad<D, ROWS, NT>::CH; ++n) t.issue(n);
 }
 
 // Enqueue 64 fp32 values (rows [0, nrows) valid, stride `st` elements) into
