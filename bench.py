@@ -61,11 +61,13 @@ def fwd_bytes(batch) -> int:
 
 
 def kernel_fingerprint() -> str:
-    """sha256 over the HIP sources, as recorded next to the profiled traffic."""
+    """sha256 over the HIP sources and the build script (which holds the
+    compiler flags), as recorded next to the profiled traffic."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "variable_length_attention_ragged_amd", "csrc", "*"))):
+    pkg = os.path.join(ROOT, "variable_length_attention_ragged_amd")
+    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
         h.update(os.path.basename(p).encode())
         with open(p, "rb") as f:
             h.update(f.read())
