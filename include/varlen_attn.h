@@ -71,7 +71,10 @@ enum {
   VARLEN_ATTN_ERR_WORKSPACE = 8,   /* workspace NULL or too small */
   VARLEN_ATTN_ERR_POLICY = 9,      /* default_policy not 0, 1 or 2 */
   VARLEN_ATTN_ERR_SCALE = 10,      /* scale not finite */
-  VARLEN_ATTN_ERR_HIP = 11         /* a HIP launch failed */
+  VARLEN_ATTN_ERR_HIP = 11,        /* a HIP launch failed */
+  VARLEN_ATTN_ERR_OFFSETS = 12     /* a tensor gives both `ragged` and
+                                      `ragged_scaled`, or ragged_multiplier is
+                                      outside [1, 2^31) */
 };
 
 /* Mask policies (TransformerEngine names: padding, padding_causal,
@@ -106,14 +109,28 @@ enum {
  * stride is 1.  `span_elems` is the number of elements addressable from
  * `data` (the allocation's or view's element span, not the count of valid
  * tokens: cudnn-frontend PR #462, review of the sizing helper and "Not
- * addressed here").  `ragged` holds batch + 1 int64 element offsets; entry
- * `batch` (past-the-end) is not used for addressing. */
+ * addressed here").
+ *
+ * The offset of sequence b's row 0 (in elements from `data`) is given in
+ * exactly one of two forms; entry `batch` (past-the-end) is not used for
+ * addressing:
+ *   ragged         int64 [batch + 1] element offsets, or
+ *   ragged_scaled  int32 [batch + 1] values in units of ragged_multiplier
+ *                  elements: offset = ragged_scaled[b] * ragged_multiplier,
+ *                  formed on the device (cuDNN's ragged-offset multiplier,
+ *                  cudnn-frontend issue on padded THD, "What needs
+ *                  checking").  One row-offset array such as a padded
+ *                  cu_seqlens then serves every tensor, each with its own
+ *                  multiplier (its stride_t).
+ * The unused pointer is NULL; ragged_multiplier is ignored with `ragged`. */
 typedef struct varlen_attn_tensor {
   void* data;
   int64_t span_elems;
   int64_t stride_t;
   int64_t stride_h;
   const int64_t* ragged;
+  const int32_t* ragged_scaled;
+  int64_t ragged_multiplier;
 } varlen_attn_tensor;
 
 /* The problem.  cu_seqlens_q/kv: device int32 [batch+1] cumulative valid

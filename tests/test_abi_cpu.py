@@ -35,8 +35,8 @@ def test_library_exports_every_declared_function():
     assert sorted(va.exported_symbols()) == names
 
 
-def _t(span, st, sh, data=FAKE):
-    return B.varlen_attn_tensor(data, span, st, sh, FAKE)
+def _t(span, st, sh, data=FAKE, ragged=FAKE, scaled=None, mult=0):
+    return B.varlen_attn_tensor(data, span, st, sh, ragged, scaled, mult)
 
 
 def _p(batch=2, h_q=4, h_kv=2, d=128, scale=0.1, policy=0, mask=None):
@@ -61,6 +61,8 @@ def _fwd(p, q=None, k=None, v=None, o=None, lse=None, ws=FAKE, ws_bytes=1 << 30)
     ("null_q", B.ERR_NULL), ("align", B.ERR_ALIGN), ("stride8", B.ERR_STRIDE),
     ("stride_small", B.ERR_STRIDE), ("span", B.ERR_SPAN), ("workspace", B.ERR_WORKSPACE),
     ("ws_align", B.ERR_ALIGN), ("ws_null", B.ERR_WORKSPACE),
+    ("no_offsets", B.ERR_NULL), ("both_offsets", B.ERR_OFFSETS),
+    ("multiplier0", B.ERR_OFFSETS), ("multiplier_big", B.ERR_OFFSETS),
 ])
 def test_host_validation_codes(case, code):
     p = _p()
@@ -93,8 +95,27 @@ def test_host_validation_codes(case, code):
         kw["ws"] = FAKE + 64
     elif case == "ws_null":
         kw["ws"] = None
+    elif case == "no_offsets":
+        kw["k"] = _t(100 * 256, 256, 128, ragged=None)
+    elif case == "both_offsets":
+        kw["k"] = _t(100 * 256, 256, 128, scaled=FAKE, mult=256)
+    elif case == "multiplier0":
+        kw["v"] = _t(100 * 256, 256, 128, ragged=None, scaled=FAKE, mult=0)
+    elif case == "multiplier_big":
+        kw["o"] = _t(100 * 512, 512, 128, ragged=None, scaled=FAKE, mult=1 << 31)
     assert _fwd(p, **kw) == code
     assert va.status_string(code) != "unknown status code"
+
+
+def test_scaled_offsets_pass_host_validation():
+    """Row-unit offsets with a multiplier are a complete alternative to
+    element offsets: such tensors pass every tensor check, so the call gets
+    as far as the workspace check (and, with batch 0, succeeds with no
+    launch)."""
+    k = _t(100 * 256, 256, 128, ragged=None, scaled=FAKE, mult=256)
+    lse = _t(100 * 4, 4, 1, ragged=None, scaled=FAKE, mult=4)
+    assert _fwd(_p(), k=k, lse=lse, ws=None) == B.ERR_WORKSPACE
+    assert _fwd(_p(batch=0), k=k, lse=lse, ws=None, ws_bytes=0) == B.OK
 
 
 def test_empty_batch_is_a_no_op():

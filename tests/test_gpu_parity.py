@@ -28,9 +28,9 @@ def _gpu():
     va.lib()  # fail loudly if the library is missing
 
 
-def _dev(batch, with_grad=None):
+def _dev(batch, with_grad=None, **kw):
     from workloads.device import DeviceBatch
-    return DeviceBatch(batch, with_grad=with_grad)
+    return DeviceBatch(batch, with_grad=with_grad, **kw)
 
 
 # ------------------------------------------------------------------ setup kernel
@@ -252,6 +252,57 @@ def test_bad_device_arguments_set_status_and_leave_outputs_untouched():
                            t["dk"], t["dv"])
     for n in ("dq", "dk", "dv"):
         compare_bf16(batch, n, dev.host(n), bref[n], bref[n + "_written"], GRAD_TOL, rel=GRAD_REL)
+
+
+@pytest.mark.parametrize("seed", [310, 311])
+def test_scaled_row_offsets_fwd_bwd(seed):
+    """Offsets given as int32 row numbers times each tensor's token stride (one
+    row array per side, shared by every tensor on it) address exactly what the
+    int64 element offsets address: outputs are bit-identical to the
+    element-offset run and match the oracle."""
+    batch = workloads.random_batch(seed, batch=7, max_len=300, h_q=4, h_kv=2, dim=128,
+                                   q_causal_offset=bool(seed % 2))
+    say(f"[scaled] seed={seed}")
+    elem = _dev(batch)
+    elem.fwd()
+    elem.bwd()
+    sc = _dev(batch, scaled_offsets=True)
+    assert sc.rows["q"] is sc.rows["o"] and sc.rows["k"] is sc.rows["dv"]
+    sc.fwd()
+    sc.bwd()
+    torch.cuda.synchronize()
+    assert int(sc.status.item()) == int(elem.status.item()) == 0
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(sc.flat[n].view(torch.int16 if n != "lse" else torch.int32),
+                           elem.flat[n].view(torch.int16 if n != "lse" else torch.int32)), n
+    check_forward(batch, sc)
+    check_backward(batch, sc)
+
+
+def test_scaled_offset_multiplier_is_applied_on_device():
+    """The multiplier is applied by the setup kernel, before its offset checks:
+    a Q multiplier of stride + 4 puts every sequence that starts on an odd row
+    off the 16-byte grid (status BAD_OFFSET, outputs untouched) and moves the
+    others to the rows the product names, exactly as the oracle reads them."""
+    # packed rows (no NaN pad rows between sequences): the shifted rows of the
+    # sequences that stay valid then read real data
+    batch = workloads.random_batch(330, batch=6, max_len=60, zero_lengths=False, max_gap=0,
+                                   token_gaps=False, h_q=2, h_kv=2, dim=64)
+    lay_q = batch.layouts["q"]
+    m = lay_q.stride_t + 4
+    starts = lay_q.start_rows[:-1]
+    assert (starts % 2 == 1).any() and (starts % 2 == 0).any()
+    dev = _dev(batch, scaled_offsets=True)
+    dev.rows["q"] = dev.rows["q"].clone()   # Q alone gets the odd multiplier
+    dev.multiplier["q"] = m
+    dev.fwd()
+    torch.cuda.synchronize()
+    prob, t = oracle.from_batch(batch)
+    t["q"].ragged = lay_q.start_rows.astype(np.int64) * m
+    ref = oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"])
+    assert ref["status"] & oracle.ST_BAD_OFFSET
+    assert int(dev.status.item()) == ref["status"]
+    compare_bf16(batch, "o", dev.host("o"), ref["o"], ref["o_written"], O_TOL)
 
 
 def test_workspace_guard_bands():

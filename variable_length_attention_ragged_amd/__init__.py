@@ -43,24 +43,36 @@ def view_span(t: torch.Tensor) -> int:
 
 @dataclass
 class Ragged:
-    """A ragged tensor: strided view + device element offsets [batch+1].
+    """A ragged tensor: strided view + device offsets [batch+1] of each
+    sequence's row 0.
 
-    ``span`` overrides the addressable element count (default: the view's
-    span); use it when the caller's allocation extends past the view."""
+    The offsets are either int64 element offsets (``ragged``) or int32
+    values in units of ``multiplier`` elements (``scaled``), e.g. one padded
+    cu_seqlens array shared by every tensor with multiplier = its token
+    stride; give one of them.  ``span`` overrides the addressable element
+    count (default: the view's span); use it when the caller's allocation
+    extends past the view."""
 
     view: torch.Tensor
-    ragged: torch.Tensor
+    ragged: torch.Tensor | None = None
     span: int | None = None
+    scaled: torch.Tensor | None = None
+    multiplier: int = 0
 
     def c(self) -> varlen_attn_tensor:
         v = self.view
-        if self.ragged.dtype != torch.int64:
+        if self.ragged is not None and self.ragged.dtype != torch.int64:
             raise TypeError("ragged offsets must be int64")
+        if self.scaled is not None and self.scaled.dtype != torch.int32:
+            raise TypeError("scaled offsets must be int32")
         st, sh = v.stride(0), v.stride(1)
         if v.dim() == 3 and v.stride(2) != 1:
             raise ValueError("the innermost (head_dim) stride must be 1")
-        return varlen_attn_tensor(v.data_ptr(), self.span if self.span is not None else view_span(v),
-                                  st, sh, self.ragged.data_ptr())
+        return varlen_attn_tensor(
+            v.data_ptr(), self.span if self.span is not None else view_span(v), st, sh,
+            self.ragged.data_ptr() if self.ragged is not None else None,
+            self.scaled.data_ptr() if self.scaled is not None else None,
+            self.multiplier if self.scaled is not None else 0)
 
 
 @dataclass

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libvarlen_attn.so")
 OK = 0
 ERR_NULL, ERR_BATCH, ERR_HEAD_DIM, ERR_HEADS, ERR_ALIGN, ERR_STRIDE = 1, 2, 3, 4, 5, 6
 ERR_SPAN, ERR_WORKSPACE, ERR_POLICY, ERR_SCALE, ERR_HIP = 7, 8, 9, 10, 11
+ERR_OFFSETS = 12
 # mask policies
 PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 # device status bits
@@ -26,7 +27,8 @@ ST_NEG_LENGTH, ST_BAD_OFFSET, ST_OUT_OF_SPAN, ST_BAD_POLICY, ST_LIST_OVERFLOW = 
 
 class varlen_attn_tensor(ctypes.Structure):
     _fields_ = [("data", c_void_p), ("span_elems", c_int64), ("stride_t", c_int64),
-                ("stride_h", c_int64), ("ragged", c_void_p)]
+                ("stride_h", c_int64), ("ragged", c_void_p), ("ragged_scaled", c_void_p),
+                ("ragged_multiplier", c_int64)]
 
 
 class varlen_attn_problem(ctypes.Structure):

@@ -49,7 +49,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Checks a tensor descriptor; `elem` is its element size, `dim` elements per
 // (row, head), `heads` its head count.
 int check_tensor(const varlen_attn_tensor* t, int heads, int dim, int elem) {
-  if (!t || !t->data || !t->ragged) return VARLEN_ATTN_ERR_NULL;
+  if (!t || !t->data || (!t->ragged && !t->ragged_scaled)) return VARLEN_ATTN_ERR_NULL;
+  if (t->ragged && t->ragged_scaled) return VARLEN_ATTN_ERR_OFFSETS;
+  if (t->ragged_scaled && (t->ragged_multiplier < 1 || t->ragged_multiplier >= (int64_t(1) << 31)))
+    return VARLEN_ATTN_ERR_OFFSETS;
   const bool bf16 = elem == 2;
   if (bf16 && ((uintptr_t)t->data % 16) != 0) return VARLEN_ATTN_ERR_ALIGN;
   if (!bf16 && ((uintptr_t)t->data % 4) != 0) return VARLEN_ATTN_ERR_ALIGN;
@@ -141,6 +144,8 @@ DevTensor dev_tensor(const varlen_attn_tensor* t, int heads, int dim, int align)
   d.st = t->stride_t;
   d.sh = t->stride_h;
   d.ragged = t->ragged;
+  d.ragged32 = t->ragged ? nullptr : t->ragged_scaled;
+  d.mult = t->ragged ? 1 : t->ragged_multiplier;
   d.heads = heads;
   d.dim = dim;
   d.align = align;
@@ -453,6 +458,8 @@ const char* varlen_attn_status_string(int code) {
     case VARLEN_ATTN_ERR_POLICY: return "default_policy must be 0, 1 or 2";
     case VARLEN_ATTN_ERR_SCALE: return "scale must be finite";
     case VARLEN_ATTN_ERR_HIP: return "a HIP kernel launch failed";
+    case VARLEN_ATTN_ERR_OFFSETS:
+      return "give exactly one of ragged / ragged_scaled, with ragged_multiplier in [1, 2^31)";
     default: return "unknown status code";
   }
 }

@@ -30,7 +30,9 @@ struct DevTensor {
   int64_t span;
   int64_t st;
   int64_t sh;
-  const int64_t* ragged;
+  const int64_t* ragged;    // element offsets, or null when ragged32 is used
+  const int32_t* ragged32;  // offsets in units of `mult` elements
+  int64_t mult;
   int32_t heads;
   int32_t dim;     // D for bf16 tensors, 1 for LSE
   int32_t align;   // required element alignment of ragged offsets

@@ -29,6 +29,12 @@ constexpr int kLdsSeq = 1024;
 
 __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Element offset of sequence b's row 0: given directly, or as a scaled int32
+// value times the tensor's multiplier (formed here, on the device).
+__device__ inline int64_t offset_of(const DevTensor& t, int b) {
+  return t.ragged ? t.ragged[b] : (int64_t)t.ragged32[b] * t.mult;
+}
+
 __device__ int check_tensor(const DevTensor& t, int64_t base, int64_t rows) {
   if (base < 0 || (base % t.align) != 0) return VARLEN_ATTN_ST_BAD_OFFSET;
   // The host guarantees (heads-1)*sh + dim <= span, so `extra` < span and
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
       const DevTensor& t = a.t[id];
       if (!t.present) continue;
       const int64_t rows = is_query_side(id) ? lq : lk;
-      if (rows > 0) st |= check_tensor(t, t.ragged[b], rows);
+      if (rows > 0) st |= check_tensor(t, offset_of(t, b), rows);
     }
     const bool causal =
         pol == VARLEN_ATTN_CAUSAL_TOP_LEFT || pol == VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT;
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     w.diag[b] = (int32_t)diag;
     w.flags[b] = (valid ? 1 : 0) | (st << 8);
     for (int id = 0; id < T_COUNT; ++id)
-      w.base[(int64_t)id * B + b] = a.t[id].present ? a.t[id].ragged[b] : 0;
+      w.base[(int64_t)id * B + b] = a.t[id].present ? offset_of(a.t[id], b) : 0;
     cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, causal, diag, a.bm, a.bn) : 0;
     cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, causal, diag, a.bm_b, a.bn_b) : 0;
     if (st) atomicOr(&s_status, st);

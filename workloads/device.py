@@ -17,9 +17,16 @@ OUTPUTS = ("o", "lse", "dq", "dk", "dv")
 
 
 class DeviceBatch:
-    def __init__(self, batch: Batch, device="cuda", with_grad: bool | None = None):
+    """``scaled_offsets``: pass each tensor's offsets as int32 row numbers times
+    a multiplier (its token stride) instead of int64 element offsets; tensors
+    on one side (query or key) whose rows start at the same numbers share one
+    row array."""
+
+    def __init__(self, batch: Batch, device="cuda", with_grad: bool | None = None,
+                 scaled_offsets: bool = False):
         self.batch = batch
         self.device = device
+        self.scaled_offsets = scaled_offsets
         with_grad = ("do" in batch.data) if with_grad is None else with_grad
         self.flat = {}
         for n in ("q", "k", "v", "do"):
@@ -31,6 +38,16 @@ class DeviceBatch:
             self.flat[n] = self.fresh_output(n)
         self.ragged = {n: torch.from_numpy(lay.ragged.astype(np.int64)).to(device)
                        for n, lay in batch.layouts.items()}
+        self.rows = {}
+        self.multiplier = {n: lay.stride_t for n, lay in batch.layouts.items()}
+        if scaled_offsets:
+            shared = {}
+            for n, lay in batch.layouts.items():
+                key = tuple(int(x) for x in lay.start_rows)
+                if key not in shared:
+                    shared[key] = torch.from_numpy(
+                        np.asarray(lay.start_rows, dtype=np.int32)).to(device)
+                self.rows[n] = shared[key]
         self.cu_q = torch.from_numpy(batch.cu_q).to(device)
         self.cu_kv = torch.from_numpy(batch.cu_kv).to(device)
         self.policy = None if batch.policy is None else torch.from_numpy(batch.policy).to(device)
@@ -56,6 +73,9 @@ class DeviceBatch:
         else:
             view = torch.as_strided(flat, (lay.rows, lay.heads, lay.dim),
                                     (lay.stride_t, lay.stride_h, 1))
+        if self.scaled_offsets:
+            return va.Ragged(view, None, span=lay.span, scaled=self.rows[n],
+                             multiplier=self.multiplier[n])
         return va.Ragged(view, self.ragged[n], span=lay.span)
 
     def fwd(self, **kw):
