@@ -34,7 +34,7 @@ def from_batch(batch, outputs: dict | None = None):
     import workloads
 
     prob = Problem(batch.h_q, batch.h_kv, batch.dim, batch.scale, batch.cu_q, batch.cu_kv,
-                   batch.policy, batch.default_policy, batch.q_causal_offset)
+                   batch.policy, batch.default_policy, batch.q_causal_offset, batch.window)
     t = {}
     for n, lay in batch.layouts.items():
         if n in batch.data:

@@ -25,6 +25,13 @@ What is computed, and where the pages fix it
   absolute key index of the segment's local q[0]).  The policy is chosen per
   sequence (TransformerEngine PR #3274, "Description" and the reviewer's
   padding/causal/bottom-right mapping).
+* Sliding window (same PR, "Description": a window size per mask type beside
+  the per-sequence policy).  Policy p may carry a window (left_p, right_p),
+  -1 meaning unbounded on that side.  With the anchor ``a_b`` (the key index
+  of the sequence's row 0: ``q_causal_offset[b]`` when given, else 0 for
+  top-left and ``Lk - Lq`` for bottom-right and padding), key j is further
+  restricted to ``i + a_b - left <= j`` and ``j <= i + a_b + right`` for the
+  bounded sides.  The rule intersects with the causal one.
 * Forward (textbook definition, no online softmax):
   ``S = scale * Q_b K_bT``; masked entries -inf; ``LSE_i = M_i + ln sum_j
   exp(S_ij - M_i)``; ``P = exp(S - LSE)``; ``O = P V_b``.
@@ -38,8 +45,11 @@ Readings where the pages are silent (each listed in the design notes):
   softmax scale is an input (default 1/sqrt(D)); LSE is the natural-log
   log-sum-exp of the scaled, masked scores; a row with no allowed key is dead:
   O = 0, LSE = -inf, dQ = 0 and no dK/dV contribution; elements outside valid
-  rows are never written; ``q_causal_offset`` overrides the alignment of causal
-  sequences only; GQA groups are contiguous (kv head = h // (H_q // H_kv)).
+  rows are never written; ``q_causal_offset`` moves the diagonal of causal
+  sequences (a padding sequence has none); GQA groups are contiguous (kv head = h // (H_q // H_kv));
+  windows of padding sequences anchor bottom-right (so self-attention windows
+  are centred on the row), and ``q_causal_offset``, when given, anchors the
+  windows of every policy.
 
 The oracle may work on blocks of query rows and skip key columns masked for
 every row of the block; each row's softmax is still computed whole, so this is
@@ -119,6 +129,7 @@ class Problem:
     policy: np.ndarray | None        # int8 [B]
     default_policy: int
     q_causal_offset: np.ndarray | None  # int32 [B]
+    window: np.ndarray | None = None    # int32 [3, 2]: (left, right) per policy, -1 unbounded
 
     @property
     def batch(self) -> int:
@@ -132,6 +143,8 @@ class SeqInfo:
     policy: int
     diag: int        # causal diagonal delta_b (0 for padding)
     status: int      # OR of ST_* bits for this sequence
+    win_lo: int | None = None  # window: keys j >= i + win_lo (None: unbounded)
+    win_hi: int | None = None  # window: keys j <= i + win_hi (None: unbounded)
 
     @property
     def valid(self) -> bool:
@@ -175,7 +188,20 @@ def sequence_info(prob: Problem, q_side: list, kv_side: list, b: int) -> SeqInfo
             diag = int(prob.q_causal_offset[b])
         elif pol == CAUSAL_BOTTOM_RIGHT:
             diag = lk - lq
-    return SeqInfo(lq, lk, pol, diag, st)
+    win_lo = win_hi = None
+    if prob.window is not None and pol in (PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT):
+        left, right = (int(x) for x in prob.window[pol])
+        if prob.q_causal_offset is not None:
+            anchor = int(prob.q_causal_offset[b])
+        elif pol == CAUSAL_TOP_LEFT:
+            anchor = 0
+        else:
+            anchor = lk - lq
+        if left >= 0:
+            win_lo = anchor - left
+        if right >= 0:
+            win_hi = anchor + right
+    return SeqInfo(lq, lk, pol, diag, st, win_lo, win_hi)
 
 
 def allowed(info: SeqInfo, rows: np.ndarray, keys: np.ndarray) -> np.ndarray:
@@ -184,20 +210,36 @@ def allowed(info: SeqInfo, rows: np.ndarray, keys: np.ndarray) -> np.ndarray:
     keep = np.broadcast_to(keep, (rows.size, keys.size))
     if info.causal:
         keep = keep & (keys[None, :] <= rows[:, None] + info.diag)
+    if info.win_hi is not None:
+        keep = keep & (keys[None, :] <= rows[:, None] + info.win_hi)
+    if info.win_lo is not None:
+        keep = keep & (keys[None, :] >= rows[:, None] + info.win_lo)
     return keep
 
 
 def _key_limit(info: SeqInfo, row_end: int) -> int:
     """Keys at or beyond this index are masked for every row < row_end."""
-    if not info.causal:
-        return info.lk
-    return int(np.clip(row_end - 1 + info.diag + 1, 0, info.lk))
+    last = info.lk - 1
+    if info.causal:
+        last = min(last, row_end - 1 + info.diag)
+    if info.win_hi is not None:
+        last = min(last, row_end - 1 + info.win_hi)
+    return int(np.clip(last + 1, 0, info.lk))
 
 
-def _softmax_block(info: SeqInfo, scale: float, qb: np.ndarray, kb: np.ndarray, r0: int):
-    """Scores, LSE and probabilities for query rows r0.. of one head."""
+def _key_start(info: SeqInfo, row_start: int) -> int:
+    """Keys below this index are masked for every row >= row_start."""
+    if info.win_lo is None:
+        return 0
+    return int(np.clip(row_start + info.win_lo, 0, info.lk))
+
+
+def _softmax_block(info: SeqInfo, scale: float, qb: np.ndarray, kb: np.ndarray, r0: int,
+                   k0: int = 0):
+    """Scores, LSE and probabilities for query rows r0.. of one head against
+    keys k0.. (the keys outside [k0, k0 + len(kb)) being masked for these rows)."""
     rows = np.arange(r0, r0 + qb.shape[0])
-    keys = np.arange(kb.shape[0])
+    keys = np.arange(k0, k0 + kb.shape[0])
     s = scale * (qb @ kb.T)
     keep = allowed(info, rows, keys)
     s = np.where(keep, s, -np.inf)
@@ -240,12 +282,13 @@ def forward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Tens
             g = h // group
             for r0 in range(0, info.lq, ROW_BLOCK):
                 r1 = min(info.lq, r0 + ROW_BLOCK)
-                kl = _key_limit(info, r1)
+                ks, kl = _key_start(info, r0), _key_limit(info, r1)
+                kl = max(kl, ks)
                 qb = _gather(q, int(q.ragged[b]) + r0 * q.stride_t, r1 - r0, h)
-                kb = _gather(k, int(k.ragged[b]), kl, g)
-                vb = _gather(v, int(v.ragged[b]), kl, g)
-                lse_b, p = _softmax_block(info, prob.scale, qb, kb, r0)
-                ob = p @ vb if kl > 0 else np.zeros((r1 - r0, prob.head_dim))
+                kb = _gather(k, int(k.ragged[b]) + ks * k.stride_t, kl - ks, g)
+                vb = _gather(v, int(v.ragged[b]) + ks * v.stride_t, kl - ks, g)
+                lse_b, p = _softmax_block(info, prob.scale, qb, kb, r0, ks)
+                ob = p @ vb if kl > ks else np.zeros((r1 - r0, prob.head_dim))
                 oi = o.index(int(o.ragged[b]) + r0 * o.stride_t, r1 - r0, h)
                 o_out[oi] = ob
                 o_w[oi] = True
@@ -265,13 +308,14 @@ def forward_rows(prob: Problem, q: Tensor, k: Tensor, v: Tensor, b: int, h: int,
     out_o = np.zeros((rows.size, prob.head_dim))
     out_l = np.full(rows.size, -np.inf)
     for n, i in enumerate(rows):
-        kl = _key_limit(info, int(i) + 1)
+        ks, kl = _key_start(info, int(i)), _key_limit(info, int(i) + 1)
+        kl = max(kl, ks)
         qi = _gather(q, int(q.ragged[b]) + int(i) * q.stride_t, 1, h)
-        kb = _gather(k, int(k.ragged[b]), kl, g)
-        vb = _gather(v, int(v.ragged[b]), kl, g)
-        lse_i, p = _softmax_block(info, prob.scale, qi, kb, int(i))
+        kb = _gather(k, int(k.ragged[b]) + ks * k.stride_t, kl - ks, g)
+        vb = _gather(v, int(v.ragged[b]) + ks * v.stride_t, kl - ks, g)
+        lse_i, p = _softmax_block(info, prob.scale, qi, kb, int(i), ks)
         out_l[n] = lse_i[0]
-        if kl > 0:
+        if kl > ks:
             out_o[n] = (p @ vb)[0]
     return out_o, out_l
 
@@ -318,24 +362,25 @@ def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Ten
                 for r0 in range(0, info.lq, ROW_BLOCK):
                     r1 = min(info.lq, r0 + ROW_BLOCK)
                     n = r1 - r0
-                    kl = _key_limit(info, r1)
+                    ks, kl = _key_start(info, r0), _key_limit(info, r1)
                     qb = _gather(q, int(q.ragged[b]) + r0 * q.stride_t, n, h)
                     dob = _gather(do, int(do.ragged[b]) + r0 * do.stride_t, n, h)
                     dqi = dq.index(int(dq.ragged[b]) + r0 * dq.stride_t, n, h)
                     dq_w[dqi] = True
-                    if kl == 0:
+                    if kl <= ks:
                         dq_out[dqi] = 0.0
                         continue
-                    kb = _gather(k, int(k.ragged[b]), kl, g)
-                    vb = _gather(v, int(v.ragged[b]), kl, g)
-                    _, p = _softmax_block(info, prob.scale, qb, kb, r0)
+                    kb = _gather(k, int(k.ragged[b]) + ks * k.stride_t, kl - ks, g)
+                    vb = _gather(v, int(v.ragged[b]) + ks * v.stride_t, kl - ks, g)
+                    _, p = _softmax_block(info, prob.scale, qb, kb, r0, ks)
                     ob = p @ vb
                     delta = (dob * ob).sum(axis=1)
                     dp = dob @ vb.T
                     ds = p * (dp - delta[:, None])
                     dq_out[dqi] = prob.scale * (ds @ kb)
-                    dk_acc[dk.index(int(dk.ragged[b]), kl, g)] += prob.scale * (ds.T @ qb)
-                    dv_acc[dv.index(int(dv.ragged[b]), kl, g)] += p.T @ dob
+                    dk_acc[dk.index(int(dk.ragged[b]) + ks * dk.stride_t, kl - ks, g)] += \
+                        prob.scale * (ds.T @ qb)
+                    dv_acc[dv.index(int(dv.ragged[b]) + ks * dv.stride_t, kl - ks, g)] += p.T @ dob
     dk_out[dk_w] = dk_acc[dk_w]
     dv_out[dv_w] = dv_acc[dv_w]
     return dict(dq=dq_out, dq_written=dq_w, dk=dk_out, dk_written=dk_w,

@@ -10,16 +10,23 @@ need the read a previous change removed), with one base per tensor (the
 metadata must widen beyond one cu_q/cu_k pair).  The list format and its order
 are this library's own design:
 
-* Per sequence b: ``lq, lk, policy, diag, flags`` (int32) and one int64 base
-  per tensor in the order Q, K, V, O, LSE, dO, dQ, dK, dV (backward-only bases
-  are 0 in a forward setup).  ``flags`` = 1 if the sequence is valid, plus its
-  status bits shifted left by 8.
+* Per sequence b: ``lq, lk, policy, hi, lo, flags`` (int32) and one int64
+  base per tensor in the order Q, K, V, O, LSE, dO, dQ, dK, dV (backward-only
+  bases are 0 in a forward setup).  ``flags`` = 1 if the sequence is valid,
+  plus its status bits shifted left by 8.  ``hi`` and ``lo`` fold the causal
+  diagonal and the window into one band: key j is visible to row i iff
+  ``i + lo <= j <= i + hi`` and ``j < lk``.  ``hi`` is the smallest of the
+  causal diagonal (causal policies) and the window's upper offset (when
+  bounded), ``lk`` when neither applies; ``lo`` is the window's lower offset,
+  ``-lq`` when unbounded; both clamped to [-lq, lk], which changes no
+  visibility and keeps them in int32.  Invalid sequences store 0 for both.
 * Forward tile list (one int32 pair (b, t) per tile of ``bm`` query rows):
   valid sequences with ``lq > 0``, ordered by descending cost then ascending b,
   each sequence's tiles from last to first.  The cost of a sequence is the sum
-  over its tiles of ``max(1, ceil(kv_end / bn))``, ``kv_end`` being the key
-  bound of the tile's last row (``lk`` for padding; ``clamp(row_end + diag, 0,
-  lk)`` for causal).
+  over its tiles of ``max(1, ceil(kv_end / bn) - floor(kv_begin / bn))``, the
+  key range of the tile being ``kv_begin = clamp(row_start + lo, 0, lk)`` (its
+  first row's lower bound) to ``kv_end = clamp(row_end + hi, 0, lk)`` (its last
+  row's upper bound plus one).
 * Backward kv-tile list (int32 quadruple (b_first, n_members, u, lk_max) per
   tile of ``bn_b`` key rows of a kv group): a kv group is a maximal run of
   consecutive valid sequences with ``lk > 0`` whose K, V, dK and dV bases are
@@ -35,8 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, ST_LIST_OVERFLOW,
-                        Problem, Tensor, sequence_info)
+from .attention import ST_LIST_OVERFLOW, Problem, SeqInfo, Tensor, sequence_info
 
 BASE_ORDER = ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")
 
@@ -51,12 +57,27 @@ def rows_capacity(t: Tensor) -> int:
     return (t.span - 1 - extra) // t.stride_t + 1
 
 
-def tile_cost(lq: int, lk: int, causal: bool, diag: int, bm: int, bn: int) -> int:
+def band(info: SeqInfo) -> tuple:
+    """(hi, lo) of a sequence as the device table stores them."""
+    if not info.valid:
+        return 0, 0
+    hi = info.lk
+    if info.causal:
+        hi = min(hi, info.diag)
+    if info.win_hi is not None:
+        hi = min(hi, info.win_hi)
+    lo = -info.lq if info.win_lo is None else info.win_lo
+    clamp = lambda x: min(max(x, -info.lq), info.lk)
+    return clamp(hi), clamp(lo)
+
+
+def tile_cost(lq: int, lk: int, hi: int, lo: int, bm: int, bn: int) -> int:
     cost = 0
     for t in range(ceil_div(lq, bm)):
         row_end = min(lq, (t + 1) * bm)
-        kv_end = lk if not causal else min(max(row_end + diag, 0), lk)
-        cost += max(1, ceil_div(kv_end, bn))
+        kv_end = min(max(row_end + hi, 0), lk)
+        kv_begin = min(max(t * bm + lo, 0), lk)
+        cost += max(1, ceil_div(kv_end, bn) - kv_begin // bn)
     return cost
 
 
@@ -74,7 +95,8 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
     lq = np.zeros(B, np.int32)
     lk = np.zeros(B, np.int32)
     pol = np.zeros(B, np.int32)
-    diag = np.zeros(B, np.int32)
+    hi = np.zeros(B, np.int32)
+    lo = np.zeros(B, np.int32)
     flags = np.zeros(B, np.int32)
     base = np.zeros((9, B), np.int64)
     status = 0
@@ -82,7 +104,8 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
     for b in range(B):
         info = sequence_info(prob, q_side, kv_side, b)
         infos.append(info)
-        lq[b], lk[b], pol[b], diag[b] = info.lq, info.lk, info.policy, info.diag
+        lq[b], lk[b], pol[b] = info.lq, info.lk, info.policy
+        hi[b], lo[b] = band(info)
         flags[b] = (1 if info.valid else 0) | (info.status << 8)
         status |= info.status
         for i, n in enumerate(BASE_ORDER):
@@ -90,9 +113,7 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
                 base[i, b] = int(tensors[n].ragged[b])
 
     def cost_of(b, tm, tn):
-        i = infos[b]
-        return tile_cost(i.lq, i.lk, i.policy in (CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT),
-                         i.diag, tm, tn)
+        return tile_cost(infos[b].lq, infos[b].lk, int(hi[b]), int(lo[b]), tm, tn)
 
     listed = [b for b in range(B) if infos[b].valid and infos[b].lq > 0]
     order = sorted(listed, key=lambda b: (-cost_of(b, bm, bn), b))
@@ -126,7 +147,7 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
     if len(fwd) > cap_fwd or (backward and len(bwd) > cap_bwd):
         status |= ST_LIST_OVERFLOW
         fwd, bwd = [], []
-    return dict(lq=lq, lk=lk, policy=pol, diag=diag, flags=flags, base=base,
+    return dict(lq=lq, lk=lk, policy=pol, hi=hi, lo=lo, flags=flags, base=base,
                 fwd=np.asarray(fwd, np.int32).reshape(-1, 2),
                 bwd=np.asarray(bwd, np.int32).reshape(-1, 4),
                 status=status, infos=infos)

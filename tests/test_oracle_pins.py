@@ -350,11 +350,15 @@ def _fd_problem():
     return prob, q, k, v, o, lse, do, dq, dk, dv
 
 
-@pytest.mark.parametrize("use_offsets", [False, True])
-def test_backward_matches_central_differences(use_offsets):
+@pytest.mark.parametrize("use_offsets,windowed", [(False, False), (True, False), (True, True),
+                                                  (False, True)])
+def test_backward_matches_central_differences(use_offsets, windowed):
     prob, q, k, v, o, lse, do, dq, dk, dv = _fd_problem()
     if use_offsets:
         prob.q_causal_offset = np.array([-1, 1, 1, 3], np.int32)
+    if windowed:
+        # top-left: one key back; bottom-right: the diagonal and two keys back
+        prob.window = np.array([[-1, -1], [1, 0], [2, -1]], np.int32)
 
     def loss():
         r = oracle.forward(prob, q, k, v, o, lse)
@@ -441,3 +445,177 @@ def test_token_major_span_identities(T, h, d):
     for shape, strides in (((T, h), (1, T)), ((T, h, d), (d, T * d, 1)), ((T, h, d), (3 * h * d, d, 1))):
         assert oracle.sizing.span_by_enumeration(shape, strides) == \
             oracle.sizing.span_of_extremes(shape, strides)
+
+
+# ----------------------------------------------------------------- sliding window
+
+NO_WINDOW = np.full((3, 2), -1, np.int32)
+
+
+def _window(pad=(-1, -1), tl=(-1, -1), br=(-1, -1)):
+    return np.array([pad, tl, br], np.int32)
+
+
+def _tiny_w(lq, lk, policy, window, qco=None, dim=8, seed=3):
+    return workloads.build("tiny", seed, 1, 1, dim, [lq], [lk], [0, lq], [0, lk],
+                           default_policy=policy,
+                           q_causal_offset=None if qco is None else [qco], window=window)
+
+
+@pytest.mark.parametrize("seed,qco", [(31, False), (32, True), (33, True)])
+def test_unbounded_or_wide_window_is_no_window(seed, qco):
+    kw = dict(batch=5, max_len=40, dim=16, q_causal_offset=qco)
+    ref = _run_fwd(workloads.random_batch(seed, **kw))
+    for win in (NO_WINDOW, np.full((3, 2), 10 ** 6, np.int32)):
+        res = _run_fwd(workloads.random_batch(seed, window=win, **kw))
+        np.testing.assert_array_equal(res["o"], ref["o"])
+        np.testing.assert_array_equal(res["lse"], ref["lse"])
+
+
+def _vrows(batch, name):
+    return batch.layouts[name].view(oracle.bf16_bits_to_f64(batch.data[name]))[:, 0]
+
+
+@pytest.mark.parametrize("lq,lk,policy,window,qco,shift", [
+    (7, 7, oracle.PADDING, _window(pad=(0, 0)), None, 0),          # the diagonal only
+    (4, 9, oracle.PADDING, _window(pad=(0, 0)), None, 5),          # anchored at Lk - Lq
+    (7, 7, oracle.CAUSAL_TOP_LEFT, _window(tl=(0, -1)), None, 0),
+    (4, 9, oracle.CAUSAL_TOP_LEFT, _window(tl=(0, 4)), 3, 3),      # anchored at the offset
+    (4, 9, oracle.CAUSAL_BOTTOM_RIGHT, _window(br=(0, 0)), None, 5),
+    (6, 6, oracle.PADDING, _window(pad=(0, 0)), -2, -2),           # rows 0, 1 dead
+])
+def test_zero_width_window_selects_one_key(lq, lk, policy, window, qco, shift):
+    """A window of width 1: row i sees key i + shift alone, so O_i = V_{i+shift}
+    exactly and LSE_i = scale * q_i . k_{i+shift}; rows whose key falls outside
+    [0, Lk) are dead."""
+    batch = _tiny_w(lq, lk, policy, window, qco)
+    res = _run_fwd(batch)
+    q, k, v = _vrows(batch, "q"), _vrows(batch, "k"), _vrows(batch, "v")
+    o = batch.layouts["o"].view(res["o"])[:, 0]
+    lse = batch.layouts["lse"].view(res["lse"])[:, 0, 0]
+    for i in range(lq):
+        j = i + shift
+        if 0 <= j < lk:
+            np.testing.assert_array_equal(o[i], v[j])
+            assert lse[i] == pytest.approx(batch.scale * float(q[i] @ k[j]), rel=1e-15)
+        else:
+            assert np.all(o[i] == 0) and lse[i] == -np.inf
+
+
+def test_zero_width_window_gradients_closed_form():
+    """With one visible key per row the softmax is constant (P = 1): dQ = dK = 0
+    and dV_j = dO of the row that sees key j."""
+    batch = _tiny_w(4, 9, oracle.PADDING, _window(pad=(0, 0)))
+    prob, t = oracle.from_batch(batch)
+    g = oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                        t["dk"], t["dv"])
+    assert np.all(g["dq"][g["dq_written"]] == 0) and np.all(g["dk"][g["dk_written"]] == 0)
+    dv = batch.layouts["dv"].view(g["dv"])[:, 0]
+    do = _vrows(batch, "do")
+    np.testing.assert_array_equal(dv[:5], 0)
+    np.testing.assert_array_equal(dv[5:], do)
+
+
+def _band(lq, lk, policy, window, qco):
+    """Visibility from torch's band routines: tril(k) keeps j - i <= k and
+    triu(k) keeps j - i >= k; the causal part from torch's own causal masks."""
+    m = torch.ones(lq, lk, dtype=torch.bool)
+    if policy != oracle.PADDING:
+        if qco is not None:
+            m = m.tril(diagonal=int(qco))
+        elif policy == oracle.CAUSAL_TOP_LEFT:
+            m = causal_upper_left(lq, lk)._materialize()
+        else:
+            m = causal_lower_right(lq, lk)._materialize()
+    if window is not None:
+        left, right = (int(x) for x in window[policy])
+        anchor = int(qco) if qco is not None else (0 if policy == oracle.CAUSAL_TOP_LEFT
+                                                   else lk - lq)
+        if right >= 0:
+            m = m.tril(diagonal=anchor + right)
+        if left >= 0:
+            m = m.triu(diagonal=anchor - left)
+    return m
+
+
+def _torch_band_ref(batch, b, lq, lk, policy, need_grad=False):
+    q = torch.from_numpy(seq_rows(batch, "q", oracle.bf16_bits_to_f64(batch.data["q"]), b, lq))
+    k = torch.from_numpy(seq_rows(batch, "k", oracle.bf16_bits_to_f64(batch.data["k"]), b, lk))
+    v = torch.from_numpy(seq_rows(batch, "v", oracle.bf16_bits_to_f64(batch.data["v"]), b, lk))
+    q, k, v = (x.permute(1, 0, 2)[None].contiguous().requires_grad_(need_grad) for x in (q, k, v))
+    qco = None if batch.q_causal_offset is None else batch.q_causal_offset[b]
+    mask = _band(lq, lk, policy, batch.window, qco)
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=batch.scale,
+                                       enable_gqa=True)
+    kk = k.repeat_interleave(batch.h_q // batch.h_kv, dim=1)
+    scores = torch.matmul(q, kk.transpose(-1, -2).contiguous()) * batch.scale
+    lse = torch.logsumexp(scores.masked_fill(~mask, float("-inf")), dim=-1)
+    return q, k, v, o, lse, mask
+
+
+@pytest.mark.parametrize("seed,qco", [(41, False), (42, False), (43, True), (44, True)])
+def test_window_forward_matches_torch_sdpa_with_band_mask(seed, qco):
+    batch = workloads.random_batch(seed, batch=6, max_len=40, h_q=4, h_kv=2, dim=16,
+                                   q_causal_offset=qco, window="random")
+    assert batch.window is not None and (batch.window >= 0).any()
+    res = _run_fwd(batch)
+    assert res["status"] == 0
+    for b, info in enumerate(res["infos"]):
+        if info.lq == 0:
+            continue
+        o = seq_rows(batch, "o", res["o"], b, info.lq)
+        lse = seq_rows(batch, "lse", res["lse"], b, info.lq)[..., 0]
+        if info.lk == 0:
+            assert np.all(o == 0) and np.all(lse == -np.inf)
+            continue
+        _, _, _, o_t, lse_t, mask = _torch_band_ref(batch, b, info.lq, info.lk, info.policy)
+        live = mask.any(dim=1).numpy()
+        o_t = o_t[0].permute(1, 0, 2).detach().numpy()
+        lse_t = lse_t[0].permute(1, 0).detach().numpy()
+        np.testing.assert_allclose(o[live], o_t[live], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[live], lse_t[live], rtol=1e-12, atol=1e-12)
+        assert np.all(o[~live] == 0) and np.all(lse[~live] == -np.inf)
+
+
+@pytest.mark.parametrize("seed,qco", [(51, False), (52, True), (53, False)])
+def test_window_backward_matches_torch_autograd(seed, qco):
+    batch = workloads.random_batch(seed, batch=4, max_len=24, h_q=4, h_kv=2, dim=8,
+                                   zero_lengths=False, q_causal_offset=qco, window="random")
+    prob, t = oracle.from_batch(batch)
+    res = oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                          t["dk"], t["dv"])
+    assert res["status"] == 0
+    for b, info in enumerate(res["infos"]):
+        q, k, v, o_t, _, mask = _torch_band_ref(batch, b, info.lq, info.lk, info.policy, True)
+        do = torch.from_numpy(seq_rows(batch, "do", oracle.bf16_bits_to_f64(batch.data["do"]),
+                                       b, info.lq)).permute(1, 0, 2)[None]
+        live = mask.any(dim=1)
+        (o_t * do * live[None, None, :, None]).sum().backward()
+        dq = seq_rows(batch, "dq", res["dq"], b, info.lq)
+        dk = seq_rows(batch, "dk", res["dk"], b, info.lk)
+        dv = seq_rows(batch, "dv", res["dv"], b, info.lk)
+        np.testing.assert_allclose(dq, q.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(dk, k.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(dv, v.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
+
+
+def _pairs(lq, lk, policy, window, qco=None):
+    prob = oracle.Problem(1, 1, 8, 1.0, np.array([0, lq], np.int32), np.array([0, lk], np.int32),
+                          None, policy, None if qco is None else np.array([qco], np.int32),
+                          window)
+    info = oracle.sequence_info(prob, [], [], 0)
+    return int(oracle.attention.allowed(info, np.arange(lq), np.arange(lk)).sum())
+
+
+@pytest.mark.parametrize("L,w", [(1, 0), (5, 0), (5, 2), (9, 3), (9, 8), (9, 20)])
+def test_window_pair_counts_closed_form(L, w):
+    # causal with w keys back: row i sees min(i, w) + 1 keys
+    causal = L * (L + 1) // 2 if L <= w + 1 else (w + 1) * (w + 2) // 2 + (L - w - 1) * (w + 1)
+    assert _pairs(L, L, oracle.CAUSAL_TOP_LEFT, _window(tl=(w, 0))) == causal
+    assert _pairs(L, L, oracle.CAUSAL_BOTTOM_RIGHT, _window(br=(w, -1))) == causal
+    # symmetric padding window: 2w + 1 keys per row minus the ones cut off at
+    # either end, w(w+1)/2 per end
+    sym = L * L if L <= w else L * (2 * w + 1) - w * (w + 1)
+    assert _pairs(L, L, oracle.PADDING, _window(pad=(w, w))) == sym
+    # a causal right window adds nothing to the diagonal
+    assert _pairs(L, L, oracle.CAUSAL_TOP_LEFT, _window(tl=(w, 3))) == causal

@@ -45,7 +45,9 @@ def test_forward_and_backward_lists_by_hand():
                                  [0, 1, 0, 5], [0, 1, 1, 5], [0, 1, 2, 5],
                                  [2, 1, 0, 7], [2, 1, 1, 7], [2, 1, 2, 7], [2, 1, 3, 7],
                                  [1, 1, 0, 2]]
-    assert s["diag"].tolist() == [0, 0, 4, 0]
+    # band (hi, lo): causal diagonal or lk above, -lq below (no windows)
+    assert s["hi"].tolist() == [0, 2, 4, 4]
+    assert s["lo"].tolist() == [-5, 0, -3, -9]
     assert s["flags"].tolist() == [1, 1, 1, 1]
     assert s["base"][0].tolist() == [0, 40, 40, 64]          # Q rows 0, 5, 5, 8 (x 8)
     assert s["base"][4].tolist() == [0, 5, 5, 8]             # LSE token stride 1
@@ -80,3 +82,44 @@ def test_rows_capacity():
     assert worklist.rows_capacity(t) == 13
     hm = oracle.Tensor(np.zeros(8 * 7360, np.float32), 1, 7360, np.zeros(2, np.int64), 8, 1)
     assert worklist.rows_capacity(hm) == 7360
+
+
+def test_window_bands_and_costs_by_hand():
+    # b0: top-left causal, lq = lk = 10, window (3, 0): hi = 0, lo = -3.
+    #   bm = 4, bn = 2; tiles: rows 0-3 keys [0, 4) -> 2; rows 4-7 keys [1, 8)
+    #   -> 4 - 0 = 4; rows 8-9 keys [5, 10) -> 5 - 2 = 3              => 9
+    # b1: padding, lq = lk = 6, window (1, 1) anchored at lk - lq = 0: hi = 1,
+    #   lo = -1; rows 0-3 keys [0, 5) -> 3; rows 4-5 keys [3, 6) -> 3 - 1 = 2
+    #                                                                  => 5
+    # b2: bottom-right, lq = 2, lk = 9, window (-1, 5): the diagonal 7 binds
+    #   before the window's upper offset 7 + 5: hi = 7; lo = -lq = -2; rows
+    #   0-1 keys [0, 9) -> 5                                            => 5
+    prob = _problem([10, 6, 2], [10, 6, 9], [1, 0, 2])
+    prob.window = np.array([[1, 1], [3, 0], [-1, 5]], np.int32)
+    t = _tensors([0, 10, 16, 18], [0, 10, 16, 25], 18, 25)
+    s = worklist.setup(prob, t, backward=False, bm=4, bn=2, cap_fwd=100)
+    assert s["status"] == 0
+    assert s["hi"].tolist() == [0, 1, 7]
+    assert s["lo"].tolist() == [-3, -1, -2]
+    assert s["fwd"].tolist() == [[0, 2], [0, 1], [0, 0], [1, 1], [1, 0], [2, 0]]
+
+
+def test_window_lower_offset_and_clamps_by_hand():
+    # One padding sequence lq = 3, lk = 4 with window (0, -1): anchor lk - lq =
+    # 1, so row i sees keys >= i + 1: lo = 1, hi = lk = 4.
+    prob = _problem([3], [4], [0])
+    prob.window = np.array([[0, -1], [-1, -1], [-1, -1]], np.int32)
+    t = _tensors([0, 3], [0, 4], 3, 4)
+    s = worklist.setup(prob, t, backward=False, bm=4, bn=2, cap_fwd=100)
+    assert (s["hi"].tolist(), s["lo"].tolist()) == ([4], [1])
+    # A window far past the keys: lo = 100 clamps to lk = 4 (nothing visible);
+    # one far before them: hi = -100 clamps to -lq = -3.
+    prob.window = np.array([[-1, -1], [-1, -1], [-1, -1]], np.int32)
+    prob.q_causal_offset = np.array([103], np.int32)
+    prob.window[0] = [3, -1]
+    s = worklist.setup(prob, t, backward=False, bm=4, bn=2, cap_fwd=100)
+    assert (s["hi"].tolist(), s["lo"].tolist()) == ([4], [4])
+    prob.q_causal_offset = np.array([-103], np.int32)
+    prob.window[0] = [-1, 3]
+    s = worklist.setup(prob, t, backward=False, bm=4, bn=2, cap_fwd=100)
+    assert (s["hi"].tolist(), s["lo"].tolist()) == ([-3], [-3])

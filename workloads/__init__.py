@@ -140,6 +140,7 @@ class Batch:
     q_causal_offset: np.ndarray | None  # int32 [B] or None
     layouts: dict = field(default_factory=dict)   # q k v o lse do dq dk dv
     data: dict = field(default_factory=dict)      # q k v do -> flat uint16
+    window: np.ndarray | None = None  # int32 [3, 2] (left, right) per policy, -1 unbounded
 
     @property
     def batch(self) -> int:
@@ -167,7 +168,7 @@ def _with_gaps(lengths, gaps) -> np.ndarray:
 
 def build(name, seed, h_q, h_kv, dim, lq, lk, q_start, kv_start, *, default_policy,
           policy=None, q_causal_offset=None, lse_kind="token", scale=None,
-          q_rows=None, kv_rows=None, token_gaps=None, with_grad=True) -> Batch:
+          q_rows=None, kv_rows=None, token_gaps=None, with_grad=True, window=None) -> Batch:
     """Assemble a batch from lengths and start rows.
 
     ``token_gaps`` maps tensor name -> n, giving that tensor a token stride of
@@ -190,7 +191,7 @@ def build(name, seed, h_q, h_kv, dim, lq, lk, q_start, kv_start, *, default_poli
               lq, lk, int(default_policy),
               None if policy is None else np.asarray(policy, np.int8),
               None if q_causal_offset is None else np.asarray(q_causal_offset, np.int32),
-              lay, {})
+              lay, {}, None if window is None else np.asarray(window, np.int32).reshape(3, 2))
     g = torch.Generator().manual_seed(seed)
     b.data["q"] = fill_buffer(lay["q"], lq, g)
     b.data["k"] = fill_buffer(lay["k"], lk, g)
@@ -263,11 +264,14 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
                  dim: int = 64, cross: bool = True, max_gap: int = 40, token_gaps: bool = True,
                  policies=(PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT), per_seq_policy=True,
                  q_causal_offset: bool = False, lse_kind: str | None = None,
-                 zero_lengths: bool = True, with_grad: bool = True) -> Batch:
+                 zero_lengths: bool = True, with_grad: bool = True,
+                 window=None) -> Batch:
     """A small random ragged batch for parity tests: random lengths (some 0),
     random row gaps between sequences (separately for the query-side and
     key-side buffers), random per-tensor token-stride gaps n*H*D (n = 0..3),
-    random per-sequence policies and LSE layout."""
+    random per-sequence policies and LSE layout.  ``window``: None, an int32
+    [3, 2] array of per-policy (left, right) windows, or "random" (each side
+    unbounded with probability 1/3, else uniform in [0, max_len // 2])."""
     rng = np.random.default_rng(seed)
     lo = 0 if zero_lengths else 1
     lq = rng.integers(lo, max_len, size=batch, endpoint=True)
@@ -287,8 +291,20 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
     qco = None
     if q_causal_offset:
         qco = rng.integers(-max_len // 4, max_len + 1, size=batch).astype(np.int32)
+    if isinstance(window, str):
+        assert window == "random"
+        window = random_window(rng, max_len // 2)
     return build(f"random_{seed}", seed, h_q, h_kv, dim, lq, lk, q_start, kv_start,
                  default_policy=int(pol[0]), policy=pol if per_seq_policy else None,
                  q_causal_offset=qco, lse_kind=lse_kind, token_gaps=gaps,
                  q_rows=int(q_start[-1]) + int(rng.integers(0, 8)),
-                 kv_rows=int(kv_start[-1]) + int(rng.integers(0, 8)), with_grad=with_grad)
+                 kv_rows=int(kv_start[-1]) + int(rng.integers(0, 8)), with_grad=with_grad,
+                 window=window)
+
+
+def random_window(rng: np.random.Generator, max_size: int) -> np.ndarray:
+    """Per-policy (left, right) windows: each side -1 (unbounded) with
+    probability 1/3, else uniform in [0, max_size]."""
+    w = rng.integers(0, max_size, size=(3, 2), endpoint=True)
+    w[rng.integers(0, 3, size=(3, 2)) == 0] = -1
+    return w.astype(np.int32)
