@@ -28,6 +28,12 @@
  *   Lk(b) - Lq(b)        for VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT,
  *   q_causal_offset[b]   for either causal policy when that array is given
  *                        (the absolute key index of the segment's q[0]).
+ * Sliding window (TransformerEngine PR #3274, "Description": a window size
+ * per mask type beside the per-sequence policy): policy p may carry a window
+ * (left_p, right_p), -1 meaning unbounded on that side.  With the anchor
+ * a(b) = q_causal_offset[b] when given, else 0 for top-left and Lk(b) - Lq(b)
+ * for bottom-right and padding, key j is further restricted to
+ * i + a(b) - left_p <= j <= i + a(b) + right_p on the bounded sides.
  * A row with no visible key is dead: O = 0, LSE = -inf, dQ = 0.
  *
  * LSE is the natural-log log-sum-exp of the scaled, masked scores, fp32, in
@@ -72,9 +78,10 @@ enum {
   VARLEN_ATTN_ERR_POLICY = 9,      /* default_policy not 0, 1 or 2 */
   VARLEN_ATTN_ERR_SCALE = 10,      /* scale not finite */
   VARLEN_ATTN_ERR_HIP = 11,        /* a HIP launch failed */
-  VARLEN_ATTN_ERR_OFFSETS = 12     /* a tensor gives both `ragged` and
+  VARLEN_ATTN_ERR_OFFSETS = 12,    /* a tensor gives both `ragged` and
                                       `ragged_scaled`, or ragged_multiplier is
                                       outside [1, 2^31) */
+  VARLEN_ATTN_ERR_WINDOW = 13      /* a window_size entry below -1 */
 };
 
 /* Mask policies (TransformerEngine names: padding, padding_causal,
@@ -136,8 +143,10 @@ typedef struct varlen_attn_tensor {
 /* The problem.  cu_seqlens_q/kv: device int32 [batch+1] cumulative valid
  * lengths.  mask_policy: device int8 [batch] or NULL (then default_policy
  * applies to every sequence).  q_causal_offset: device int32 [batch] or NULL
- * (then each causal policy uses its own alignment).  GQA: query head h reads
- * key/value head h / (h_q / h_kv). */
+ * (then each causal policy uses its own alignment).  window_size: HOST int32
+ * [6] = {left, right} for padding, top-left, bottom-right, each >= -1 (else
+ * VARLEN_ATTN_ERR_WINDOW), read during the call only; NULL means no window
+ * for any policy.  GQA: query head h reads key/value head h / (h_q / h_kv). */
 typedef struct varlen_attn_problem {
   int32_t batch;
   int32_t h_q;
@@ -149,6 +158,7 @@ typedef struct varlen_attn_problem {
   const int8_t* mask_policy;
   int32_t default_policy;
   const int32_t* q_causal_offset;
+  const int32_t* window_size;
 } varlen_attn_problem;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned) and the tile
@@ -157,9 +167,12 @@ typedef struct varlen_attn_problem {
  * intermediate clobbered the next region's tile counter).
  *   counters  int32[64]  tile-claim counters, zeroed by the setup kernel
  *   header    int32[16]  [0] forward tiles, [1] backward tiles, [2] status
- *   seq       int32 lq[B], lk[B], policy[B], diag[B], flags[B] (flags: bit 0
- *             valid, status bits << 8), then at seq + seq_i64_offset int64
- *             base[9][B] in the order Q, K, V, O, LSE, dO, dQ, dK, dV
+ *   seq       int32 lq[B], lk[B], policy[B], hi[B], lo[B], flags[B] (flags:
+ *             bit 0 valid, status bits << 8; key j visible to row i iff
+ *             i + lo <= j <= i + hi and j < Lk, hi and lo clamped to
+ *             [-Lq, Lk], both 0 for invalid sequences), then at
+ *             seq + seq_i64_offset int64 base[9][B] in the order Q, K, V, O,
+ *             LSE, dO, dQ, dK, dV
  *   fwd_tiles int32[2 * capacity]: (b, t) for the t-th tile of fwd_block_m
  *             query rows of sequence b
  *   bwd_tiles int32[4 * capacity]: (first b, members, u, max Lk) for the u-th

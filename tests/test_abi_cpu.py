@@ -63,6 +63,7 @@ def _fwd(p, q=None, k=None, v=None, o=None, lse=None, ws=FAKE, ws_bytes=1 << 30)
     ("ws_align", B.ERR_ALIGN), ("ws_null", B.ERR_WORKSPACE),
     ("no_offsets", B.ERR_NULL), ("both_offsets", B.ERR_OFFSETS),
     ("multiplier0", B.ERR_OFFSETS), ("multiplier_big", B.ERR_OFFSETS),
+    ("window", B.ERR_WINDOW),
 ])
 def test_host_validation_codes(case, code):
     p = _p()
@@ -103,6 +104,9 @@ def test_host_validation_codes(case, code):
         kw["v"] = _t(100 * 256, 256, 128, ragged=None, scaled=FAKE, mult=0)
     elif case == "multiplier_big":
         kw["o"] = _t(100 * 512, 512, 128, ragged=None, scaled=FAKE, mult=1 << 31)
+    elif case == "window":
+        win = (ctypes.c_int32 * 6)(-1, -1, 128, 0, -1, -2)
+        p.window_size = ctypes.addressof(win)
     assert _fwd(p, **kw) == code
     assert va.status_string(code) != "unknown status code"
 
@@ -116,6 +120,16 @@ def test_scaled_offsets_pass_host_validation():
     lse = _t(100 * 4, 4, 1, ragged=None, scaled=FAKE, mult=4)
     assert _fwd(_p(), k=k, lse=lse, ws=None) == B.ERR_WORKSPACE
     assert _fwd(_p(batch=0), k=k, lse=lse, ws=None, ws_bytes=0) == B.OK
+
+
+def test_window_sizes_pass_host_validation():
+    """Windows of -1 (unbounded) and any size >= 0 are accepted: the call gets
+    as far as the workspace check."""
+    for vals in ((-1,) * 6, (0,) * 6, (5, 0, 1 << 30, 0, 0, 7)):
+        win = (ctypes.c_int32 * 6)(*vals)
+        p = _p()
+        p.window_size = ctypes.addressof(win)
+        assert _fwd(p, ws=None) == B.ERR_WORKSPACE
 
 
 def test_empty_batch_is_a_no_op():
@@ -176,6 +190,7 @@ def test_regions_are_disjoint_and_ordered():
                (L.bwd_tiles_offset, 16 * L.bwd_tiles_capacity),
                (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems),
                (L.lse_term_offset, 4 * L.delta_elems)]
+    assert L.seq_i64_offset >= 6 * 4 * 37      # lq, lk, policy, hi, lo, flags
     for (a, n), (b, _) in zip(regions, regions[1:]):
         assert a + n <= b and b % 256 == 0
     assert regions[-1][0] + regions[-1][1] <= L.total_bytes

@@ -39,7 +39,7 @@ def _read_setup(ws, L, B):
     raw = ws.cpu().numpy().view(np.uint8)
     i32 = lambda off, n: raw[off:off + 4 * n].view(np.int32)
     header = i32(L.header_offset, 16)
-    seq = i32(L.seq_offset, 5 * B).reshape(5, B)
+    seq = i32(L.seq_offset, 6 * B).reshape(6, B)
     base = raw[L.seq_offset + L.seq_i64_offset:L.seq_offset + L.seq_i64_offset + 72 * B] \
         .view(np.int64).reshape(9, B)
     fwd = i32(L.fwd_tiles_offset, 2 * int(header[0])).reshape(-1, 2)
@@ -65,8 +65,9 @@ def _check_setup(batch, backward):
     np.testing.assert_array_equal(seq[0], exp["lq"])
     np.testing.assert_array_equal(seq[1], exp["lk"])
     np.testing.assert_array_equal(seq[2], exp["policy"])
-    np.testing.assert_array_equal(seq[3], exp["diag"])
-    np.testing.assert_array_equal(seq[4], exp["flags"])
+    np.testing.assert_array_equal(seq[3], exp["hi"])
+    np.testing.assert_array_equal(seq[4], exp["lo"])
+    np.testing.assert_array_equal(seq[5], exp["flags"])
     np.testing.assert_array_equal(base, exp["base"])
     np.testing.assert_array_equal(fwd, exp["fwd"])
     if backward:
@@ -88,7 +89,19 @@ SETUP_CASES = [
     ("random_b1100", lambda: workloads.random_batch(300, batch=1100, max_len=12, max_gap=4)),
     ("random_b2200", lambda: workloads.random_batch(301, batch=2200, max_len=6, max_gap=2,
                                                     cross=False)),
+] + [(f"window{s}", (lambda s=s: workloads.random_batch(s, batch=9, max_len=600,
+                                                         q_causal_offset=bool(s % 2),
+                                                         window="random")))
+     for s in range(120, 126)] + [
+    ("cfg5_small_window", lambda: _windowed(workloads.config5(doc_len=4096, chunk=512,
+                                                              offsets=(512, 3584)),
+                                            [[-1, -1], [700, 0], [-1, -1]])),
 ]
+
+
+def _windowed(batch, window):
+    batch.window = np.asarray(window, np.int32)
+    return batch
 
 
 @pytest.mark.parametrize("name,make", SETUP_CASES, ids=[c[0] for c in SETUP_CASES])
@@ -121,6 +134,62 @@ def test_random_fwd_bwd(seed, dim):
     batch = workloads.random_batch(seed, batch=6, max_len=300, h_q=4, h_kv=2, dim=dim,
                                    q_causal_offset=(seed % 3 == 0))
     say(f"[random] seed={seed} D={dim} lq={batch.lq.tolist()} lk={batch.lk.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+WINDOWED = [(s, d) for s in range(220, 226) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("seed,dim", WINDOWED)
+def test_window_random_fwd_bwd(seed, dim):
+    """Per-policy sliding windows (random sizes, some sides unbounded) on
+    random ragged batches, with and without q_causal_offset anchoring them."""
+    batch = workloads.random_batch(seed, batch=6, max_len=500, h_q=4, h_kv=2, dim=dim,
+                                   q_causal_offset=(seed % 2 == 0), window="random")
+    say(f"[window] seed={seed} D={dim} window={batch.window.tolist()} "
+        f"lq={batch.lq.tolist()} lk={batch.lk.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+@pytest.mark.parametrize("window", [
+    [[-1, -1], [256, 0], [-1, -1]],       # causal, 256 keys back
+    [[100, 37], [-1, -1], [-1, -1]],      # padding, asymmetric around the row
+    [[0, 0], [0, 0], [0, 0]],             # one key per row
+])
+def test_sliding_window_long_sequences(window):
+    """Sequences of up to 2000 rows: the band skips most key tiles of every
+    query tile and most query tiles of every key tile."""
+    rng = np.random.default_rng(230)
+    lens = rng.integers(600, 2000, size=3, endpoint=True)
+    pol = np.array([0, 1, 0], np.int8)
+    start = np.concatenate([[0], np.cumsum(lens + 8)])
+    batch = workloads.build("long_window", 230, 4, 2, 128, lens, lens, start, start,
+                            default_policy=0, policy=pol, lse_kind="head", window=window)
+    say(f"[long window] {window} lens={lens.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+def test_window_with_aliased_kv_segments():
+    """Context-parallel chunks of one document with a causal window: the
+    caller's offsets anchor each chunk's band, and the chunks' dK/dV sum."""
+    batch = _windowed(workloads.config5(doc_len=1024, chunk=256, offsets=(256, 768)),
+                      [[-1, -1], [300, 0], [-1, -1]])
+    say("[window alias] cfg5 shape, doc 1024 chunk 256, window 300")
     dev = _dev(batch)
     dev.fwd()
     dev.bwd()

@@ -88,16 +88,29 @@ class Problem:
     mask_policy: torch.Tensor | None = None   # int8 [batch], device
     default_policy: int = PADDING
     q_causal_offset: torch.Tensor | None = None  # int32 [batch], device
+    # (left, right) per policy in the order padding, top-left, bottom-right;
+    # -1 unbounded.  Host values (six ints, flat or 3 x 2).
+    window_size: object | None = None
 
     def c(self) -> varlen_attn_problem:
         def ptr(t):
             return None if t is None else t.data_ptr()
         batch = self.cu_seqlens_q.numel() - 1
         scale = self.scale if self.scale is not None else self.head_dim ** -0.5
-        return varlen_attn_problem(batch, self.h_q, self.h_kv, self.head_dim, scale,
+        win = None
+        if self.window_size is not None:
+            vals = [int(x) for row in self.window_size for x in
+                    (row if hasattr(row, "__len__") else (row,))]
+            if len(vals) != 6:
+                raise ValueError("window_size needs (left, right) for each of the 3 policies")
+            win = (ctypes.c_int32 * 6)(*vals)
+        prob = varlen_attn_problem(batch, self.h_q, self.h_kv, self.head_dim, scale,
                                    ptr(self.cu_seqlens_q), ptr(self.cu_seqlens_kv),
                                    ptr(self.mask_policy), self.default_policy,
-                                   ptr(self.q_causal_offset))
+                                   ptr(self.q_causal_offset),
+                                   None if win is None else ctypes.addressof(win))
+        prob._window_keepalive = win  # the library reads it during the call
+        return prob
 
 
 def _stream(stream) -> int | None:

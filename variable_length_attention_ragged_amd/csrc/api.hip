@@ -78,6 +78,9 @@ int check_problem(const varlen_attn_problem* p) {
       (p->default_policy < VARLEN_ATTN_PADDING || p->default_policy > VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT))
     return VARLEN_ATTN_ERR_POLICY;
   if (p->batch > 0 && (!p->cu_seqlens_q || !p->cu_seqlens_kv)) return VARLEN_ATTN_ERR_NULL;
+  if (p->window_size)
+    for (int i = 0; i < 6; ++i)
+      if (p->window_size[i] < -1) return VARLEN_ATTN_ERR_WINDOW;
   return VARLEN_ATTN_OK;
 }
 
@@ -96,7 +99,7 @@ void base_layout(int64_t B, int64_t fwd_cap, int64_t bwd_cap, varlen_attn_layout
   L->header_offset = off;
   off += align256(16 * 4);
   L->seq_offset = off;
-  L->seq_i64_offset = align256(5 * 4 * B);
+  L->seq_i64_offset = align256(6 * 4 * B);
   off += align256(L->seq_i64_offset + (int64_t)T_COUNT * 8 * B);
   L->fwd_tiles_offset = off;
   L->fwd_tiles_capacity = fwd_cap;
@@ -123,8 +126,9 @@ WsView make_view(char* ws, const varlen_attn_layout& L, int64_t B) {
   w.lq = seq;
   w.lk = seq + B;
   w.policy = seq + 2 * B;
-  w.diag = seq + 3 * B;
-  w.flags = seq + 4 * B;
+  w.hi = seq + 3 * B;
+  w.lo = seq + 4 * B;
+  w.flags = seq + 5 * B;
   w.base = (int64_t*)(ws + L.seq_offset + L.seq_i64_offset);
   w.fwd_tiles = (int32_t*)(ws + L.fwd_tiles_offset);
   w.bwd_tiles = (int32_t*)(ws + L.bwd_tiles_offset);
@@ -196,6 +200,8 @@ void fill_setup(SetupArgs& s, const varlen_attn_problem* p, bool backward) {
   s.policy = p->mask_policy;
   s.default_policy = p->default_policy;
   s.q_causal_offset = p->q_causal_offset;
+  s.has_window = p->window_size ? 1 : 0;
+  for (int i = 0; i < 6; ++i) s.window[i] = p->window_size ? p->window_size[i] : -1;
   s.backward = backward ? 1 : 0;
   s.bm = kFwdBlockM;
   s.bn = kFwdBlockN;
@@ -456,6 +462,7 @@ const char* varlen_attn_status_string(int code) {
     case VARLEN_ATTN_ERR_SPAN: return "span_elems smaller than one row of every head";
     case VARLEN_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than the required size";
     case VARLEN_ATTN_ERR_POLICY: return "default_policy must be 0, 1 or 2";
+    case VARLEN_ATTN_ERR_WINDOW: return "window_size entries must be >= -1";
     case VARLEN_ATTN_ERR_SCALE: return "scale must be finite";
     case VARLEN_ATTN_ERR_HIP: return "a HIP kernel launch failed";
     case VARLEN_ATTN_ERR_OFFSETS:

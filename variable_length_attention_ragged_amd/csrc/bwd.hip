@@ -86,7 +86,7 @@ struct DkdvSmem {
 };
 
 struct QPos {
-  int hh, mi, qs;
+  int hh, mi, qs, end;  // end: one past the member's last row that sees the key tile
   bool done;
 };
 
@@ -134,28 +134,23 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
     }
 
   // Query tiles to visit, in order: query heads of the group, member
-  // sequences, BM-row tiles from the first row that can see key k0.
-  auto first_row = [&](int mi, int& lo) -> bool {
+  // sequences, BM-row tiles over the rows whose band reaches keys
+  // k0 .. k0+BN-1: rows k0 - hi .. k0 + BN - 1 - lo.
+  auto row_range = [&](int mi, int& qs, int& end) -> bool {
     const int b = bfirst + mi;
     const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
     if (lq <= 0 || lk <= k0) return false;
-    lo = 0;
-    if (ldm(w.policy + b) != VARLEN_ATTN_PADDING) {
-      const int64_t first = (int64_t)k0 - ldm(w.diag + b);
-      if (first >= lq) return false;
-      lo = (int)max(first, (int64_t)0);
-      lo -= lo % BM;
-    }
+    const int64_t first = max((int64_t)k0 - ldm(w.hi + b), (int64_t)0);
+    const int64_t last = min((int64_t)k0 + BN - ldm(w.lo + b), (int64_t)lq);
+    if (first >= last) return false;
+    qs = (int)first - (int)first % BM;
+    end = (int)last;
     return true;
   };
   auto seek = [&](QPos p) -> QPos {
     while (p.hh < a.group) {
       while (p.mi < members) {
-        int lo;
-        if (first_row(p.mi, lo)) {
-          p.qs = lo;
-          return p;
-        }
+        if (row_range(p.mi, p.qs, p.end)) return p;
         ++p.mi;
       }
       p.mi = 0;
@@ -166,7 +161,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   };
   auto next = [&](QPos p) -> QPos {
     p.qs += BM;
-    if (p.qs < ldm(w.lq + (bfirst + p.mi))) return p;
+    if (p.qs < p.end) return p;
     ++p.mi;
     return seek(p);
   };
@@ -205,8 +200,9 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   // accumulators start at the row term (so s*c = S*scale*log2(e) -
   // LSE*log2(e)) and dP's at -delta.  Masked pairs start at -inf, which
   // makes P and dS exactly zero: rows past the tile's end through the LDS
-  // row term, keys past lk and above the causal diagonal through `th` (keep
-  // entry r iff 32qb + 8(r/4) + r%4 >= th), applied only when `masked`.
+  // row term, keys past lk and outside the band through `th` and `tl` (keep
+  // entry r iff th <= 32qb + 8(r/4) + r%4 <= tl), applied only when
+  // `masked` (upper) and `masked_lo` (lower).
   //
   // The tile runs as four phases of 16 MFMAs each, software-pipelined by
   // hand (scheduling barriers keep the order): LDS operands are read two
@@ -215,7 +211,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   //   A  S, dP of block 0          B  S, dP of block 1   + P, dS of block 0
   //   C  dV, dK from block 0       D  dV, dK from block 1 (+ P, dS of block 1
   //                                   finishing in C)
-  auto compute = [&](auto BUF, bool masked, int th) {
+  auto compute = [&](auto BUF, bool masked, int th, bool masked_lo, int tl) {
     constexpr int buf = decltype(BUF)::value;
     const uint16_t* qt = sm.q[buf];
     const uint16_t* dt = sm.dout[buf];
@@ -241,6 +237,13 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           s[qb][r] = 32 * qb + 8 * (r >> 2) + (r & 3) >= th ? s[qb][r] : -INFINITY;
+    }
+    if (masked_lo) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[qb][r] = 32 * qb + 8 * (r >> 2) + (r & 3) <= tl ? s[qb][r] : -INFINITY;
     }
 
     // Operand streams.  Natural step i (0..2KS-1): block i/KS, ks = i%KS.
@@ -330,17 +333,17 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
     if (wave == 0 && qs + lane >= lq) sm.lt[buf][lane] = -INFINITY;
     __syncthreads();  // this tile visible to all waves; the previous one consumed
     if (!nx.done) issue(nx, buf ^ 1);
-    const bool causal = ldm(w.policy + b) != VARLEN_ATTN_PADDING;
-    const int64_t dg = ldm(w.diag + b);
+    const int64_t hi = ldm(w.hi + b), lo = ldm(w.lo + b);
+    const int64_t last = min(qs + BM, lq) - 1;  // the tile's last row
     cur = nx;
-    if (wk0 >= lk || (causal && (int64_t)wk0 > (int64_t)(qs + BM - 1) + dg)) return;
-    const bool masked = wk0 + 32 > lk || (causal && (int64_t)(wk0 + 31) > (int64_t)qs + dg);
-    int th = -1;
-    if (my_key >= lk)
-      th = BM;
-    else if (causal)
-      th = (int)min(max((int64_t)my_key - dg - qs, (int64_t)-1), (int64_t)BM);
-    compute(BUF, masked, th - 4 * hf);
+    // skip when the wave's keys are past every row's upper band edge or
+    // before every row's lower one
+    if (wk0 >= lk || wk0 > qs + BM - 1 + hi || wk0 + 31 < qs + lo) return;
+    const bool masked = wk0 + 32 > lk || wk0 + 31 > qs + hi;
+    const bool masked_lo = wk0 < last + lo;
+    const int th = my_key >= lk ? BM : (int)min(max(my_key - hi - qs, (int64_t)-1), (int64_t)BM);
+    const int tl = (int)min(max(my_key - lo - qs, (int64_t)-1), (int64_t)BM);
+    compute(BUF, masked, th - 4 * hf, masked_lo, tl - 4 * hf);
   };
 
   if (!cur.done) issue(cur, 0);
@@ -413,31 +416,28 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
   const WsView& w = a.ws;
 
   const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
-  const int64_t dg = ldm(w.diag + b);
-  const bool causal = ldm(w.policy + b) != VARLEN_ATTN_PADDING;
+  const int64_t hi = ldm(w.hi + b), lo = ldm(w.lo + b);  // band: i + lo <= key <= i + hi
   const int64_t qbase = ldm(w.base + (T_Q * B + b)), dobase = ldm(w.base + (T_DO * B + b));
   const int64_t kbase = ldm(w.base + (T_K * B + b)), vbase = ldm(w.base + (T_V * B + b));
   const int64_t lbase = ldm(w.base + (T_LSE * B + b)), dqbase = ldm(w.base + (T_DQ * B + b));
 
+  // Key tiles j0 .. j1-1 and the masks, as in the forward.
+  auto clamp_k = [&](int64_t x) -> int { return (int)min(max(x, (int64_t)0), (int64_t)lk); };
   const int q0 = t * BM;
   const int rows = min(BM, lq - q0);
-  int kv_end = lk;
-  if (causal) kv_end = (int)min(max((int64_t)(q0 + rows) + dg, (int64_t)0), (int64_t)lk);
-  const int n_kv = (kv_end + BN - 1) / BN;
+  const int j0 = clamp_k(q0 + lo) / BN;
+  const int j1 = (clamp_k(q0 + rows + hi) + BN - 1) / BN;
   const int wq0 = q0 + wave * 32;
+  const int wlast = min(wq0 + 31, lq - 1);
   const bool wave_active = wq0 < lq;
-  int wave_kv_end = kv_end;
-  if (causal)
-    wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
+  const int wave_kv_end = clamp_k(wlast + 1 + hi);
+  const int wave_kv_begin = clamp_k(wq0 + lo);
   const int i = wq0 + l32;
   const bool row_ok = i < lq;
-  // Last visible key of this lane's row and of the wave's first row.
-  auto last_key = [&](int64_t row) -> int {
-    if (!causal) return lk - 1;
-    return (int)min(max(row + dg, (int64_t)-1), (int64_t)lk - 1);
-  };
-  const int lim = last_key(i);
-  const int wave_lim = last_key(wq0);
+  const int lim = (int)min(max((int64_t)i + hi, (int64_t)-1), (int64_t)lk - 1);
+  const int first = clamp_k((int64_t)i + lo);
+  const int wave_lim = (int)min(max((int64_t)wq0 + hi, (int64_t)-1), (int64_t)lk - 1);
+  const int wave_first = clamp_k((int64_t)wlast + lo);
 
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -498,13 +498,15 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     constexpr int buf = decltype(BUF)::value;
     wait_tile_loads();
     __syncthreads();
-    if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
+    if (j + 1 < j1) load_kv(j + 1, buf ^ 1);
     const int k0 = j * BN;
-    if (!wave_active || k0 >= wave_kv_end) return;
+    if (!wave_active || k0 >= wave_kv_end || k0 + BN <= wave_kv_begin) return;
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
     const bool masked = k0 + BN - 1 > wave_lim;
-    const int th = lim - k0 - 4 * hf;  // entry (kb, r) masked when its key offset > th
+    const bool masked_lo = k0 < wave_first;
+    const int th = lim - k0 - 4 * hf;    // entry (kb, r) masked when its key offset > th
+    const int tl = first - k0 - 4 * hf;  // ... or < tl
 
     // ---- per 32-key block: S^T = K Q^T and dP^T = V dO^T, then
     //      dS^T = P^T o (dP^T - delta).  The accumulators start at the row
@@ -537,6 +539,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(sc[r] * c);
         if (masked && kb * 32 + 8 * (r >> 2) + (r & 3) > th) p = 0.f;
+        if (masked_lo && kb * 32 + 8 * (r >> 2) + (r & 3) < tl) p = 0.f;
         dp[r] = p * dp[r];
       }
 #pragma unroll
@@ -560,10 +563,10 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     }
   };
 
-  if (n_kv > 0) load_kv(0, 0);
-  for (int j = 0; j < n_kv; j += 2) {
+  if (j0 < j1) load_kv(j0, 0);
+  for (int j = j0; j < j1; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_kv) step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < j1) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (row_ok) {

@@ -56,7 +56,8 @@ struct WsView {
   int32_t* lq;
   int32_t* lk;
   int32_t* policy;
-  int32_t* diag;
+  int32_t* hi;          // key j visible to row i iff i + lo <= j <= i + hi (and j < lk)
+  int32_t* lo;
   int32_t* flags;
   int64_t* base;        // [T_COUNT][batch]
   int32_t* fwd_tiles;   // (b, t) pairs
@@ -75,6 +76,8 @@ struct SetupArgs {
   const int8_t* policy;
   int32_t default_policy;
   const int32_t* q_causal_offset;
+  int32_t window[6];    // (left, right) per policy, -1 unbounded
+  int32_t has_window;
   DevTensor t[T_COUNT];
   int32_t backward;
   int32_t bm, bn, bm_b, bn_b;

@@ -53,34 +53,34 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   const int B = a.batch;
   const WsView& w = a.ws;
 
-  const int lq = ldm(w.lq + b), lk = ldm(w.lk + b), pol = ldm(w.policy + b);
-  const int64_t dg = ldm(w.diag + b);
-  const bool causal = pol != VARLEN_ATTN_PADDING;
+  const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
+  const int64_t hi = ldm(w.hi + b), lo = ldm(w.lo + b);  // band: i + lo <= key <= i + hi
   const int64_t qbase = ldm(w.base + (T_Q * B + b)), kbase = ldm(w.base + (T_K * B + b));
   const int64_t vbase = ldm(w.base + (T_V * B + b)), obase = ldm(w.base + (T_O * B + b));
   const int64_t lbase = ldm(w.base + (T_LSE * B + b));
 
+  // Key tiles j0 .. j1-1: from the first row's lower band edge to the last
+  // row's upper one.
+  auto clamp_k = [&](int64_t x) -> int { return (int)min(max(x, (int64_t)0), (int64_t)lk); };
   const int q0 = t * BM;
   const int rows = min(BM, lq - q0);
-  int kv_end = lk;
-  if (causal) kv_end = (int)min(max((int64_t)(q0 + rows) + dg, (int64_t)0), (int64_t)lk);
-  const int n_kv = (kv_end + BN - 1) / BN;
+  const int j0 = clamp_k(q0 + lo) / BN;
+  const int j1 = (clamp_k(q0 + rows + hi) + BN - 1) / BN;
 
   const int wq0 = q0 + wave * 32;
+  const int wlast = min(wq0 + 31, lq - 1);
   const bool wave_active = wq0 < lq;
-  int wave_kv_end = kv_end;
-  if (causal)
-    wave_kv_end = (int)min(max((int64_t)min(wq0 + 32, lq) + dg, (int64_t)0), (int64_t)lk);
+  const int wave_kv_end = clamp_k(wlast + 1 + hi);
+  const int wave_kv_begin = clamp_k(wq0 + lo);
   const int i = wq0 + l32;
   const bool row_ok = i < lq;
-  // Last visible key of this lane's row and of the wave's first row (keys
-  // past it are masked), clamped to [-1, lk - 1].
-  auto last_key = [&](int64_t row) -> int {
-    if (!causal) return lk - 1;
-    return (int)min(max(row + dg, (int64_t)-1), (int64_t)lk - 1);
-  };
-  const int lim = last_key(i);
-  const int wave_lim = last_key(wq0);
+  // This lane's row sees keys first..lim; the wave needs the upper mask on
+  // tiles reaching past its first row's last key and the lower mask on tiles
+  // starting before its last row's first key.
+  const int lim = (int)min(max((int64_t)i + hi, (int64_t)-1), (int64_t)lk - 1);
+  const int first = clamp_k((int64_t)i + lo);
+  const int wave_lim = (int)min(max((int64_t)wq0 + hi, (int64_t)-1), (int64_t)lk - 1);
+  const int wave_first = clamp_k((int64_t)wlast + lo);
 
   // A negative scale is folded into Q (exact sign flip) so that the row max
   // can be taken on raw scores and c > 0.
@@ -141,9 +141,9 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
     constexpr int buf = decltype(BUF)::value;
     wait_tile_loads();  // this wave's part of tile j landed
     __syncthreads();    // all parts of tile j visible; tile j-1 fully consumed
-    if (j + 1 < n_kv) load_kv(j + 1, buf ^ 1);
+    if (j + 1 < j1) load_kv(j + 1, buf ^ 1);
     const int k0 = j * BN;
-    if (!wave_active || k0 >= wave_kv_end) return;
+    if (!wave_active || k0 >= wave_kv_end || k0 + BN <= wave_kv_begin) return;
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
 
@@ -171,8 +171,9 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
       }
     }
 
-    // ---- mask (boundary tiles only): entry (kb, r) is key
-    //      k0 + kb*32 + 8(r/4) + 4hf + r%4, masked when past `lim`.
+    // ---- mask (band-edge tiles only): entry (kb, r) is key
+    //      k0 + kb*32 + 8(r/4) + 4hf + r%4, masked past `lim` or before
+    //      `first`.
     if (k0 + BN - 1 > wave_lim) {
       const int th = lim - k0 - 4 * hf;
 #pragma unroll
@@ -180,6 +181,14 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > th) s[kb][r] = -INFINITY;
+    }
+    if (k0 < wave_first) {
+      const int tl = first - k0 - 4 * hf;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) < tl) s[kb][r] = -INFINITY;
     }
 
     // ---- online softmax on raw scores (c > 0)
@@ -240,10 +249,10 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
     }
   };
 
-  if (n_kv > 0) load_kv(0, 0);
-  for (int j = 0; j < n_kv; j += 2) {
+  if (j0 < j1) load_kv(j0, 0);
+  for (int j = j0; j < j1; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_kv) step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < j1) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2

@@ -45,17 +45,20 @@ __device__ int check_tensor(const DevTensor& t, int64_t base, int64_t rows) {
   return (rows - 1 > room / t.st) ? VARLEN_ATTN_ST_OUT_OF_SPAN : 0;
 }
 
-// Sum over the query tiles of max(1, number of key tiles the tile reaches).
-// Lengths are below 2^31, so the divisions run in 32 bits.
-__device__ int64_t sequence_cost(int64_t lq, int64_t lk, bool causal, int64_t diag, int bm,
+// Sum over the query tiles of max(1, number of key tiles the tile reaches):
+// from its first row's lower band edge to its last row's upper one.  Lengths
+// are below 2^31, so the divisions run in 32 bits.
+__device__ int64_t sequence_cost(int64_t lq, int64_t lk, int64_t hi, int64_t lo, int bm,
                                  int bn) {
   int64_t cost = 0;
   const uint32_t n = (uint32_t)((lq + bm - 1) / bm);
   for (uint32_t t = 0; t < n; ++t) {
     const int64_t row_end = min(lq, (int64_t)(t + 1) * bm);
-    int64_t kv_end = lk;
-    if (causal) kv_end = min(max(row_end + diag, (int64_t)0), lk);
-    cost += max(1u, ((uint32_t)kv_end + (uint32_t)bn - 1) / (uint32_t)bn);
+    const int64_t kv_end = min(max(row_end + hi, (int64_t)0), lk);
+    const int64_t kv_begin = min(max((int64_t)t * bm + lo, (int64_t)0), lk);
+    const uint32_t tiles = ((uint32_t)kv_end + (uint32_t)bn - 1) / (uint32_t)bn -
+                           (uint32_t)kv_begin / (uint32_t)bn;
+    cost += max(1u, tiles);
   }
   return cost;
 }
@@ -150,23 +153,38 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     }
     const bool causal =
         pol == VARLEN_ATTN_CAUSAL_TOP_LEFT || pol == VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT;
-    int64_t diag = 0;
-    if (causal) {
-      if (a.q_causal_offset)
-        diag = a.q_causal_offset[b];
-      else if (pol == VARLEN_ATTN_CAUSAL_BOTTOM_RIGHT)
-        diag = lk - lq;
-    }
     const bool valid = st == 0;
+    // The band: key j is visible to row i iff i + lo <= j <= i + hi (and
+    // j < lk).  The causal diagonal and the window's upper edge bound hi,
+    // the window's lower edge bounds lo; an unbounded side gets a value that
+    // excludes no key, and clamping both to [-lq, lk] changes no visibility.
+    int64_t hi = lk, lo = -lq;
+    if (valid) {
+      // the key index of row 0: the caller's offset, else the alignment
+      const int64_t anchor = a.q_causal_offset ? (int64_t)a.q_causal_offset[b]
+                             : pol == VARLEN_ATTN_CAUSAL_TOP_LEFT ? 0 : lk - lq;
+      if (causal) hi = anchor;
+      if (a.has_window) {
+        const int64_t left = pol == 0 ? a.window[0] : pol == 1 ? a.window[2] : a.window[4];
+        const int64_t right = pol == 0 ? a.window[1] : pol == 1 ? a.window[3] : a.window[5];
+        if (right >= 0) hi = min(hi, anchor + right);
+        if (left >= 0) lo = anchor - left;
+      }
+      hi = min(max(hi, -lq), lk);
+      lo = min(max(lo, -lq), lk);
+    } else {
+      hi = lo = 0;
+    }
     w.lq[b] = (int32_t)lq;
     w.lk[b] = (int32_t)lk;
     w.policy[b] = pol;
-    w.diag[b] = (int32_t)diag;
+    w.hi[b] = (int32_t)hi;
+    w.lo[b] = (int32_t)lo;
     w.flags[b] = (valid ? 1 : 0) | (st << 8);
     for (int id = 0; id < T_COUNT; ++id)
       w.base[(int64_t)id * B + b] = a.t[id].present ? offset_of(a.t[id], b) : 0;
-    cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, causal, diag, a.bm, a.bn) : 0;
-    cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, causal, diag, a.bm_b, a.bn_b) : 0;
+    cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, hi, lo, a.bm, a.bn) : 0;
+    cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, hi, lo, a.bm_b, a.bn_b) : 0;
     if (st) atomicOr(&s_status, st);
     if (valid && lq > 0) atomicAdd(&s_listed, 1);
   }
