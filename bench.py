@@ -27,24 +27,44 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
+# --workload: (workloads function, description)
+WORKLOADS = {
+    "packed_causal": ("config2", "packed causal THD: 16 sequences, lengths U[128,4096] "
+                                 "(seed 1002), H_q=H_kv=32, D=128, top-left causal, "
+                                 "head-major LSE; fwd+bwd"),
+    "sliding_window": ("config2_window", "packed causal THD with a sliding window: the "
+                                         "packed causal lengths (seed 1002), H_q=H_kv=32, "
+                                         "D=128, top-left causal, window (1024, 0), "
+                                         "head-major LSE; fwd+bwd"),
+}
+
 
 def pairs_per_head(batch) -> np.ndarray:
-    """Allowed (query, key) pairs of each sequence, per head."""
+    """Allowed (query, key) pairs of each sequence, per head: row i sees the
+    keys first(i) .. last(i) of [0, Lk), bounded by the causal diagonal and
+    the policy's window."""
     out = np.zeros(batch.batch, np.int64)
     for b in range(batch.batch):
         lq, lk = int(batch.lq[b]), int(batch.lk[b])
         pol = int(batch.policy[b]) if batch.policy is not None else batch.default_policy
         if lq <= 0 or lk <= 0:
             continue
-        if pol == 0:
-            out[b] = lq * lk
-            continue
         if batch.q_causal_offset is not None:
-            d = int(batch.q_causal_offset[b])
+            anchor = int(batch.q_causal_offset[b])
         else:
-            d = 0 if pol == 1 else lk - lq
+            anchor = 0 if pol == 1 else lk - lq
         i = np.arange(lq, dtype=np.int64)
-        out[b] = int(np.clip(i + d + 1, 0, lk).sum())
+        first = np.zeros(lq, np.int64)
+        last = np.full(lq, lk - 1, np.int64)
+        if pol != 0:
+            last = np.minimum(last, i + anchor)
+        if batch.window is not None:
+            left, right = (int(x) for x in batch.window[pol])
+            if right >= 0:
+                last = np.minimum(last, i + anchor + right)
+            if left >= 0:
+                first = np.maximum(first, i + anchor - left)
+        out[b] = int(np.clip(last - first + 1, 0, None).sum())
     return out
 
 
@@ -74,11 +94,11 @@ def kernel_fingerprint() -> str:
     return h.hexdigest()
 
 
-def profiled_traffic(kernel: str):
+def profiled_traffic(kernel: str, workload: str):
     """Calibrated HBM bytes per launch of `kernel` from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload, or None when
     the kernel sources have changed since those counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic__packed_causal_h32_d128.json")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic__{workload}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -125,6 +145,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="packed_causal",
+                    help="packed_causal (the headline configuration) or sliding_window "
+                         "(the same lengths with a causal window of 1024 keys back)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibrates HBM byte counters against a known size) and exit")
@@ -154,7 +177,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
         return 0
-    batch = workloads.config2(with_grad=True)
+    batch = getattr(workloads, WORKLOADS[args.workload][0])(with_grad=True)
     dev = DeviceBatch(batch, with_grad=True)
     fwd_ws = torch.empty(dev.fwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
     bwd_ws = torch.empty(dev.bwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
@@ -227,8 +250,7 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "packed causal THD: 16 sequences, lengths U[128,4096] (seed 1002), "
-                        "H_q=H_kv=32, D=128, top-left causal, head-major LSE; fwd+bwd",
+            "workload": WORKLOADS[args.workload][1],
             "tokens": int(batch.lq.sum()),
             "pairs_per_head": pairs,
             "fwd_gflop": round(fwd_flops / 1e9, 2),
@@ -251,7 +273,7 @@ def main(argv=None) -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": profiled_traffic(dominant),
+            "traffic": profiled_traffic(dominant, batch.name),
         },
         "cpu_baseline": None,
     }

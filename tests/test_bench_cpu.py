@@ -1,0 +1,35 @@
+"""The benchmark's work count against the oracle's mask (no GPU needed)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+@pytest.mark.parametrize("seed,qco,window", [(700, False, None), (701, True, None),
+                                             (702, False, "random"), (703, True, "random"),
+                                             (704, True, "random")])
+def test_pairs_per_head_counts_the_oracle_mask(seed, qco, window):
+    batch = workloads.random_batch(seed, batch=8, max_len=90, q_causal_offset=qco,
+                                   window=window, with_grad=False)
+    prob, t = oracle.from_batch(batch)
+    got = bench.pairs_per_head(batch)
+    for b in range(batch.batch):
+        info = oracle.sequence_info(prob, [], [], b)
+        if info.lq <= 0 or info.lk <= 0:
+            assert got[b] == 0
+            continue
+        mask = oracle.attention.allowed(info, np.arange(info.lq), np.arange(info.lk))
+        assert got[b] == int(mask.sum()), b
+
+
+def test_bench_workloads_are_the_named_configurations():
+    full = workloads.config2()
+    win = workloads.config2_window()
+    assert np.array_equal(full.lq, win.lq) and full.window is None
+    assert win.window.tolist() == [[-1, -1], [1024, 0], [-1, -1]]
+    # the window removes pairs of rows more than 1024 keys past their sequence start
+    assert bench.pairs_per_head(win).sum() < bench.pairs_per_head(full).sum()

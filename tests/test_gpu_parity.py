@@ -448,6 +448,28 @@ def test_full_size_forward_sampled(cfg):
     _check_pads_untouched(batch, dev, ("o", "lse"))
 
 
+def test_full_size_sliding_window_sampled():
+    """The benchmark's sliding-window workload at full size, in the launch
+    configuration the benchmark times: sampled forward rows and the complete
+    gradients of one kv head."""
+    batch = workloads.config2_window(with_grad=True)
+    say(f"[full window] B={batch.batch} lq_sum={int(batch.lq.sum())} window={batch.window.tolist()}")
+    dev = _dev(batch, with_grad=True)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    assert int(dev.status.item()) == 0
+    _check_sampled_fwd(batch, dev, seed=12)
+    ref = oracle_bwd(batch, kv_heads=[7])
+    for n in ("dq", "dk", "dv"):
+        w = ref[n + "_written"]
+        g = bf16_to_f64(dev.host(n)[w])
+        err = np.abs(g - ref[n][w]).max()
+        say(f"  {n}: max abs err {err:.3e} over {int(w.sum())} elements")
+        assert err <= GRAD_TOL
+    _check_pads_untouched(batch, dev, ("o", "lse", "dq", "dk", "dv"))
+
+
 @pytest.mark.parametrize("cfg,kv_heads", [(3, [0, 5]), (5, [3])])
 def test_full_size_backward_head_subset(cfg, kv_heads):
     batch = workloads.CONFIGS[cfg](with_grad=True)

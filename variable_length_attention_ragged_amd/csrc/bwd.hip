@@ -410,7 +410,8 @@ template <int D>
 __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int h, int g) {
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16, DB = D / 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar band tests
   const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
   const WsView& w = a.ws;
@@ -506,7 +507,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     const bool masked = k0 + BN - 1 > wave_lim;
     const bool masked_lo = k0 < wave_first;
     const int th = lim - k0 - 4 * hf;    // entry (kb, r) masked when its key offset > th
-    const int tl = first - k0 - 4 * hf;  // ... or < tl
+    const int tl = first - k0 - 4 * hf;  // ... or < tl (tl <= 0 unless masked_lo)
 
     // ---- per 32-key block: S^T = K Q^T and dP^T = V dO^T, then
     //      dS^T = P^T o (dP^T - delta).  The accumulators start at the row
@@ -535,12 +536,17 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
           dp = mfma32(va[ks & 1], df[ks], dp);
         }
       }
+      // P, with the band edges masked on edge tiles only
+      if (masked || masked_lo) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sc[r] * c);
-        if (masked && kb * 32 + 8 * (r >> 2) + (r & 3) > th) p = 0.f;
-        if (masked_lo && kb * 32 + 8 * (r >> 2) + (r & 3) < tl) p = 0.f;
-        dp[r] = p * dp[r];
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const float p = fast_exp2(sc[r] * c);
+          dp[r] = (off > th || off < tl) ? 0.f : p * dp[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = fast_exp2(sc[r] * c) * dp[r];
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {

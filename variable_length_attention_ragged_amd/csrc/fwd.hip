@@ -48,7 +48,8 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-wide blocks of head_dim
   constexpr float kRescale = 8.f;  // log2 headroom before the running max is raised
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar band tests
   const int hf = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int B = a.batch;
   const WsView& w = a.ws;

@@ -222,6 +222,15 @@ def config2(seed: int = 1002, with_grad: bool = False) -> Batch:
                  default_policy=CAUSAL_TOP_LEFT, lse_kind="head", with_grad=with_grad)
 
 
+def config2_window(seed: int = 1002, with_grad: bool = False, left: int = 1024) -> Batch:
+    """The packed causal workload with a bounded causal window: each row sees
+    itself and the ``left`` keys before it (the lengths and data of config 2)."""
+    b = config2(seed, with_grad)
+    b.name = f"packed_causal_window{left}_h32_d128"
+    b.window = np.array([[-1, -1], [left, 0], [-1, -1]], np.int32)
+    return b
+
+
 def config3(seed: int = 1003, with_grad: bool = True) -> Batch:
     rng = np.random.default_rng(seed)
     lens = rng.integers(64, 2048, size=32, endpoint=True)
