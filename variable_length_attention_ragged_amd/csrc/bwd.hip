@@ -428,6 +428,12 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
   const int rows = min(BM, lq - q0);
   const int j0 = clamp_k(q0 + lo) / BN;
   const int j1 = (clamp_k(q0 + rows + hi) + BN - 1) / BN;
+  const int n_kv = max(j1 - j0, 0);
+  const int rot = band_rotation(j0, j1, hi, lo, BM, BN);
+  auto tile_of = [&](int n) {  // key tile of step n
+    const int x = n + rot;
+    return j0 + (x >= n_kv ? x - n_kv : x);
+  };
   const int wq0 = q0 + wave * 32;
   const int wlast = min(wq0 + 31, lq - 1);
   const bool wave_active = wq0 < lq;
@@ -495,12 +501,12 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  auto step = [&](auto BUF, int j) {
+  auto step = [&](auto BUF, int n) {
     constexpr int buf = decltype(BUF)::value;
     wait_tile_loads();
     __syncthreads();
-    if (j + 1 < j1) load_kv(j + 1, buf ^ 1);
-    const int k0 = j * BN;
+    if (n + 1 < n_kv) load_kv(tile_of(n + 1), buf ^ 1);
+    const int k0 = tile_of(n) * BN;
     if (!wave_active || k0 >= wave_kv_end || k0 + BN <= wave_kv_begin) return;
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
@@ -569,10 +575,10 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     }
   };
 
-  if (j0 < j1) load_kv(j0, 0);
-  for (int j = j0; j < j1; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < j1) step(std::integral_constant<int, 1>{}, j + 1);
+  if (n_kv > 0) load_kv(tile_of(0), 0);
+  for (int n = 0; n < n_kv; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 < n_kv) step(std::integral_constant<int, 1>{}, n + 1);
   }
 
   if (row_ok) {

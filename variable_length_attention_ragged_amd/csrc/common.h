@@ -131,6 +131,25 @@ enum Stage : unsigned {
   STAGE_BWD_DQ = 16u,
 };
 
+// Key-tile order of a query tile whose band starts past key 0: the walk over
+// tiles j0..j1-1 starts at the multiple of P (the tile count of a band that
+// no sequence edge clips) inside the range and wraps around, so every query
+// tile of the sequence reads key tile j at step j mod P.  Tiles running side
+// by side then read the same K/V tiles at the same time and hit in L2; in
+// natural order they read 2 tiles apart, which on 64 workgroups per XCD
+// re-reads about an L2's worth of data between two uses.  Online softmax
+// does not depend on the order.  Returns the offset to add to the step
+// index (mod the tile count); 0 keeps the natural order.
+__device__ __forceinline__ int band_rotation(int j0, int j1, int64_t hi, int64_t lo, int bm,
+                                             int bn) {
+  if (j0 <= 0) return 0;
+  // hi and lo lie in [-2^31, 2^31), so the tile counts fit 32 bits
+  const int lo_tiles = (int)(lo >= 0 ? lo / bn : -((-lo + bn - 1) / bn));  // floor(lo / bn)
+  const int period = (int)((bm + hi + bn - 1) / bn) - lo_tiles;            // >= 1 since hi >= lo
+  const int r = (int)(((int64_t)j0 + period - 1) / period) * period;
+  return r < j1 ? r - j0 : 0;
+}
+
 // Number of workgroups a persistent launch should use on the current device.
 int persistent_grid(const void* kernel, int threads, size_t lds_bytes);
 

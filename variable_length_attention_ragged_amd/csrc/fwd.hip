@@ -67,6 +67,12 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   const int rows = min(BM, lq - q0);
   const int j0 = clamp_k(q0 + lo) / BN;
   const int j1 = (clamp_k(q0 + rows + hi) + BN - 1) / BN;
+  const int n_kv = max(j1 - j0, 0);
+  const int rot = band_rotation(j0, j1, hi, lo, BM, BN);
+  auto tile_of = [&](int n) {  // key tile of step n
+    const int x = n + rot;
+    return j0 + (x >= n_kv ? x - n_kv : x);
+  };
 
   const int wq0 = q0 + wave * 32;
   const int wlast = min(wq0 + 31, lq - 1);
@@ -138,12 +144,12 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
 
   // One K/V tile; BUF is a compile-time buffer index so that every LDS
   // address is a lane register plus an immediate.
-  auto step = [&](auto BUF, int j) {
+  auto step = [&](auto BUF, int n) {
     constexpr int buf = decltype(BUF)::value;
-    wait_tile_loads();  // this wave's part of tile j landed
-    __syncthreads();    // all parts of tile j visible; tile j-1 fully consumed
-    if (j + 1 < j1) load_kv(j + 1, buf ^ 1);
-    const int k0 = j * BN;
+    wait_tile_loads();  // this wave's part of step n's tile landed
+    __syncthreads();    // all parts of it visible; step n-1's tile fully consumed
+    if (n + 1 < n_kv) load_kv(tile_of(n + 1), buf ^ 1);
+    const int k0 = tile_of(n) * BN;
     if (!wave_active || k0 >= wave_kv_end || k0 + BN <= wave_kv_begin) return;
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
@@ -250,10 +256,10 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
     }
   };
 
-  if (j0 < j1) load_kv(j0, 0);
-  for (int j = j0; j < j1; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < j1) step(std::integral_constant<int, 1>{}, j + 1);
+  if (n_kv > 0) load_kv(tile_of(0), 0);
+  for (int n = 0; n < n_kv; n += 2) {
+    step(std::integral_constant<int, 0>{}, n);
+    if (n + 1 < n_kv) step(std::integral_constant<int, 1>{}, n + 1);
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
