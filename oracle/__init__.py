@@ -13,14 +13,14 @@ Modules:
 """
 from .attention import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, PADDING, ST_BAD_OFFSET,
                         ST_BAD_POLICY, ST_LIST_OVERFLOW, ST_NEG_LENGTH, ST_OUT_OF_SPAN,
-                        Problem, Tensor, backward, bf16_bits_to_f64, forward, forward_rows,
-                        sequence_info)
+                        Problem, Tensor, backward, bf16_bits_to_f64, bits_to_f64, forward,
+                        forward_rows, sequence_info)
 from . import sizing, worklist
 
 __all__ = [
     "CAUSAL_BOTTOM_RIGHT", "CAUSAL_TOP_LEFT", "PADDING", "ST_BAD_OFFSET", "ST_BAD_POLICY",
     "ST_LIST_OVERFLOW", "ST_NEG_LENGTH", "ST_OUT_OF_SPAN", "Problem", "Tensor", "backward",
-    "bf16_bits_to_f64", "forward", "forward_rows", "sequence_info", "sizing", "worklist",
+    "bf16_bits_to_f64", "bits_to_f64", "forward", "forward_rows", "sequence_info", "sizing", "worklist",
     "from_batch",
 ]
 
@@ -42,7 +42,7 @@ def from_batch(batch, outputs: dict | None = None):
         elif outputs is not None and n in outputs:
             data = outputs[n]
         else:
-            data = workloads.out_buffer(lay, "f32" if n == "lse" else "bf16")
+            data = workloads.out_buffer(lay, "f32" if n == "lse" else batch.dtype)
         t[n] = Tensor(np.asarray(data), lay.stride_t, lay.stride_h, lay.ragged, lay.heads,
-                      lay.dim)
+                      lay.dim, batch.dtype)
     return prob, t

@@ -76,6 +76,16 @@ ST_LIST_OVERFLOW = 1 << 4  # more tiles than the output buffer can hold
 ROW_BLOCK = 512
 
 
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE binary16 bit patterns (uint16) to float64."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of 16-bit patterns of `dtype` ("bf16" or "f16")."""
+    return bf16_bits_to_f64(bits) if dtype == "bf16" else f16_bits_to_f64(bits)
+
+
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (uint16) to float64."""
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -85,12 +95,13 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 class Tensor:
     """A ragged tensor as the caller binds it: flat buffer + strides + offsets."""
 
-    data: np.ndarray        # flat: uint16 bf16 bits, float32 (LSE) or float64
+    data: np.ndarray        # flat: uint16 bf16/fp16 bits, float32 (LSE) or float64
     stride_t: int
     stride_h: int
     ragged: np.ndarray      # int64 [B+1] element offsets
     heads: int
-    dim: int                # D for bf16 tensors, 1 for LSE
+    dim: int                # D for 16-bit tensors, 1 for LSE
+    dtype: str = "bf16"     # element type of uint16 data: "bf16" or "f16"
 
     @property
     def span(self) -> int:
@@ -98,7 +109,7 @@ class Tensor:
 
     @property
     def align(self) -> int:
-        # bf16 rows are read 16 bytes at a time: offsets must be multiples of 8
+        # 16-bit rows are read 16 bytes at a time: offsets must be multiples of 8
         return 8 if self.data.dtype == np.uint16 else 1
 
     def index(self, base: int, rows: int, head: int) -> np.ndarray:
@@ -108,13 +119,13 @@ class Tensor:
         return base + head * self.stride_h + r + d
 
     def values(self) -> np.ndarray:
-        """Buffer contents as float64 (bf16 bit patterns widened exactly)."""
+        """Buffer contents as float64 (16-bit patterns widened exactly)."""
         return self.values_at(slice(None))
 
     def values_at(self, idx) -> np.ndarray:
-        """Elements at `idx` as float64 (bf16 bit patterns widened exactly)."""
+        """Elements at `idx` as float64 (16-bit patterns widened exactly)."""
         if self.data.dtype == np.uint16:
-            return bf16_bits_to_f64(self.data[idx])
+            return bits_to_f64(self.data[idx], self.dtype)
         return self.data[idx].astype(np.float64)
 
 

@@ -7,7 +7,6 @@ import numpy as np
 
 import oracle
 import workloads
-from tests._util import bf16_to_f64
 
 # Tolerances (max-abs vs fp64) for the HIP path.  Gradients: 5e-2 absolute,
 # plus 2^-8 of the magnitude, because a bf16 output cannot come closer to the
@@ -27,7 +26,7 @@ def say(*a):
 
 def pre_fill(batch: workloads.Batch, n: str) -> np.ndarray:
     lay = batch.layouts[n]
-    return workloads.out_buffer(lay, "f32" if n == "lse" else "bf16")
+    return workloads.out_buffer(lay, "f32" if n == "lse" else batch.dtype)
 
 
 def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what="", rel=0.0):
@@ -39,7 +38,7 @@ def compare_bf16(batch, n, gpu_bits, ref_vals, written, tol, what="", rel=0.0):
     bad = np.nonzero(gpu_bits[untouched] != pre[untouched])[0]
     assert bad.size == 0, f"{what}{n}: {bad.size} elements outside valid rows were written"
     if written.any():
-        g = bf16_to_f64(gpu_bits[written])
+        g = oracle.bits_to_f64(gpu_bits[written], batch.dtype)
         r = ref_vals[written]
         assert np.all(np.isfinite(g)), f"{what}{n}: non-finite output in a valid row"
         err = np.abs(g - r)

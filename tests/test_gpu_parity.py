@@ -419,7 +419,7 @@ def _check_sampled_fwd(batch, dev, seed):
         o_ref, l_ref = oracle.forward_rows(prob, t["q"], t["k"], t["v"], b, h, rows)
         r0 = int(batch.layouts["o"].start_rows[b])
         rl = int(batch.layouts["lse"].start_rows[b])
-        g = bf16_to_f64(o_gpu[np.asarray(rows) + r0, h])
+        g = oracle.bits_to_f64(o_gpu[np.asarray(rows) + r0, h], batch.dtype)
         err = np.abs(g - o_ref).max()
         worst = max(worst, err)
         assert err <= O_TOL, (b, h, rows, err)
@@ -463,7 +463,7 @@ def test_full_size_sliding_window_sampled():
     ref = oracle_bwd(batch, kv_heads=[7])
     for n in ("dq", "dk", "dv"):
         w = ref[n + "_written"]
-        g = bf16_to_f64(dev.host(n)[w])
+        g = oracle.bits_to_f64(dev.host(n)[w], batch.dtype)
         err = np.abs(g - ref[n][w]).max()
         say(f"  {n}: max abs err {err:.3e} over {int(w.sum())} elements")
         assert err <= GRAD_TOL
@@ -482,7 +482,7 @@ def test_full_size_backward_head_subset(cfg, kv_heads):
     ref = oracle_bwd(batch, kv_heads=kv_heads)
     for n in ("dq", "dk", "dv"):
         w = ref[n + "_written"]
-        g = bf16_to_f64(dev.host(n)[w])
+        g = oracle.bits_to_f64(dev.host(n)[w], batch.dtype)
         err = np.abs(g - ref[n][w]).max()
         mag = np.abs(ref[n][w]).max()
         say(f"  {n}: max abs err {err:.3e}, max |ref| {mag:.3e}, over {int(w.sum())} elements")

@@ -126,10 +126,16 @@ def test_mixed_policy_equals_sum_of_two_single_policy_passes():
 
 # ----------------------------------------------------------------- library routine
 
+def _torch_f64(batch, name):
+    """A 16-bit input buffer widened to float64 by torch's own conversion."""
+    t = torch.from_numpy(batch.data[name].view(np.int16)).view(workloads.TORCH_DTYPE[batch.dtype])
+    return t.double().numpy()
+
+
 def _torch_ref(batch, b, lq, lk, policy, need_grad=False):
-    q = torch.from_numpy(seq_rows(batch, "q", oracle.bf16_bits_to_f64(batch.data["q"]), b, lq))
-    k = torch.from_numpy(seq_rows(batch, "k", oracle.bf16_bits_to_f64(batch.data["k"]), b, lk))
-    v = torch.from_numpy(seq_rows(batch, "v", oracle.bf16_bits_to_f64(batch.data["v"]), b, lk))
+    q = torch.from_numpy(seq_rows(batch, "q", _torch_f64(batch, "q"), b, lq))
+    k = torch.from_numpy(seq_rows(batch, "k", _torch_f64(batch, "k"), b, lk))
+    v = torch.from_numpy(seq_rows(batch, "v", _torch_f64(batch, "v"), b, lk))
     q, k, v = (x.permute(1, 0, 2)[None].contiguous().requires_grad_(need_grad) for x in (q, k, v))
     if policy == oracle.PADDING:
         mask = torch.ones(lq, lk, dtype=torch.bool)
@@ -145,9 +151,11 @@ def _torch_ref(batch, b, lq, lk, policy, need_grad=False):
     return q, k, v, o, lse, mask
 
 
-@pytest.mark.parametrize("seed", [11, 12, 13, 14])
-def test_forward_matches_torch_sdpa_per_sequence(seed):
-    batch = workloads.random_batch(seed, batch=5, max_len=40, h_q=4, h_kv=2, dim=16)
+@pytest.mark.parametrize("seed,dtype", [(11, "bf16"), (12, "bf16"), (13, "bf16"), (14, "bf16"),
+                                        (15, "f16"), (16, "f16")])
+def test_forward_matches_torch_sdpa_per_sequence(seed, dtype):
+    batch = workloads.random_batch(seed, batch=5, max_len=40, h_q=4, h_kv=2, dim=16,
+                                   dtype=dtype)
     res = _run_fwd(batch)
     assert res["status"] == 0
     for b, info in enumerate(res["infos"]):
@@ -168,17 +176,17 @@ def test_forward_matches_torch_sdpa_per_sequence(seed):
         assert np.all(o_t[~live] == 0)                                  # torch agrees on O
 
 
-@pytest.mark.parametrize("seed", [21, 22, 23])
-def test_backward_matches_torch_autograd_per_sequence(seed):
+@pytest.mark.parametrize("seed,dtype", [(21, "bf16"), (22, "bf16"), (23, "bf16"), (24, "f16")])
+def test_backward_matches_torch_autograd_per_sequence(seed, dtype):
     batch = workloads.random_batch(seed, batch=4, max_len=24, h_q=4, h_kv=2, dim=8,
-                                   zero_lengths=False)
+                                   zero_lengths=False, dtype=dtype)
     prob, t = oracle.from_batch(batch)
     res = oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
                           t["dk"], t["dv"])
     assert res["status"] == 0
     for b, info in enumerate(res["infos"]):
         q, k, v, o_t, _, mask = _torch_ref(batch, b, info.lq, info.lk, info.policy, True)
-        do = torch.from_numpy(seq_rows(batch, "do", oracle.bf16_bits_to_f64(batch.data["do"]),
+        do = torch.from_numpy(seq_rows(batch, "do", _torch_f64(batch, "do"),
                                        b, info.lq)).permute(1, 0, 2)[None]
         live = mask.any(dim=1)
         (o_t * do * live[None, None, :, None]).sum().backward()
@@ -188,6 +196,55 @@ def test_backward_matches_torch_autograd_per_sequence(seed):
         np.testing.assert_allclose(dq, q.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
         np.testing.assert_allclose(dk, k.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
         np.testing.assert_allclose(dv, v.grad[0].permute(1, 0, 2).numpy(), rtol=1e-9, atol=1e-11)
+
+
+# ----------------------------------------------------------------- fp16 inputs
+
+def test_f16_widening_is_exact_for_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bits_to_f64(bits, "f16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # and bf16 against torch's bfloat16
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    mine = oracle.bits_to_f64(bits, "bf16")
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and np.array_equal(mine[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("seed", [81, 82])
+def test_same_values_in_either_format_give_identical_results(seed):
+    """The oracle computes in fp64 from exactly widened inputs, so a batch whose
+    values are representable in both formats gives bit-identical outputs."""
+    a = workloads.random_batch(seed, batch=4, max_len=50, dim=16, window="random",
+                               q_causal_offset=True)
+    b = workloads.random_batch(seed, batch=4, max_len=50, dim=16, window="random",
+                               q_causal_offset=True, dtype="f16")
+    for n in ("q", "k", "v", "do"):
+        vals = torch.from_numpy(a.data[n].view(np.int16)).view(torch.bfloat16).float()
+        # bf16 values below 2^-14 may not be exact in fp16: flush those to 0
+        vals = torch.where(vals.abs() < 2.0 ** -14, torch.zeros_like(vals), vals)
+        a.data[n] = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        h = vals.to(torch.float16)
+        assert torch.equal(h.float().nan_to_num(7.0), vals.nan_to_num(7.0))  # exact
+        b.data[n] = h.view(torch.int16).numpy().view(np.uint16)
+    pa, ta = oracle.from_batch(a)
+    pb, tb = oracle.from_batch(b)
+    fa = oracle.forward(pa, ta["q"], ta["k"], ta["v"], ta["o"], ta["lse"])
+    fb = oracle.forward(pb, tb["q"], tb["k"], tb["v"], tb["o"], tb["lse"])
+    w = fa["o_written"]
+    assert np.array_equal(w, fb["o_written"]) and np.array_equal(fa["o"][w], fb["o"][w])
+    lw = fa["lse_written"]
+    assert np.array_equal(fa["lse"][lw], fb["lse"][lw])
+    ga = oracle.backward(pa, ta["q"], ta["k"], ta["v"], ta["o"], ta["lse"], ta["do"], ta["dq"],
+                         ta["dk"], ta["dv"])
+    gb = oracle.backward(pb, tb["q"], tb["k"], tb["v"], tb["o"], tb["lse"], tb["do"], tb["dq"],
+                         tb["dk"], tb["dv"])
+    for n in ("dq", "dk", "dv"):
+        w = ga[n + "_written"]
+        assert np.array_equal(ga[n][w], gb[n][w]), n
 
 
 # ----------------------------------------------------------------- closed forms
@@ -539,9 +596,9 @@ def _band(lq, lk, policy, window, qco):
 
 
 def _torch_band_ref(batch, b, lq, lk, policy, need_grad=False):
-    q = torch.from_numpy(seq_rows(batch, "q", oracle.bf16_bits_to_f64(batch.data["q"]), b, lq))
-    k = torch.from_numpy(seq_rows(batch, "k", oracle.bf16_bits_to_f64(batch.data["k"]), b, lk))
-    v = torch.from_numpy(seq_rows(batch, "v", oracle.bf16_bits_to_f64(batch.data["v"]), b, lk))
+    q = torch.from_numpy(seq_rows(batch, "q", _torch_f64(batch, "q"), b, lq))
+    k = torch.from_numpy(seq_rows(batch, "k", _torch_f64(batch, "k"), b, lk))
+    v = torch.from_numpy(seq_rows(batch, "v", _torch_f64(batch, "v"), b, lk))
     q, k, v = (x.permute(1, 0, 2)[None].contiguous().requires_grad_(need_grad) for x in (q, k, v))
     qco = None if batch.q_causal_offset is None else batch.q_causal_offset[b]
     mask = _band(lq, lk, policy, batch.window, qco)
@@ -587,7 +644,7 @@ def test_window_backward_matches_torch_autograd(seed, qco):
     assert res["status"] == 0
     for b, info in enumerate(res["infos"]):
         q, k, v, o_t, _, mask = _torch_band_ref(batch, b, info.lq, info.lk, info.policy, True)
-        do = torch.from_numpy(seq_rows(batch, "do", oracle.bf16_bits_to_f64(batch.data["do"]),
+        do = torch.from_numpy(seq_rows(batch, "do", _torch_f64(batch, "do"),
                                        b, info.lq)).permute(1, 0, 2)[None]
         live = mask.any(dim=1)
         (o_t * do * live[None, None, :, None]).sum().backward()

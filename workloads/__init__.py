@@ -1,12 +1,13 @@
 """Seeded synthetic ragged THD batches shared by the tests, the bench and smoke().
 
 This module only *constructs inputs*: sequence lengths, where each sequence's
-rows live in its buffers (the caller-bound ragged offsets), bf16 bit patterns
-drawn from N(0, 1), and NaN-filled pad rows.  It holds none of the attention
+rows live in its buffers (the caller-bound ragged offsets), bf16 or fp16 bit
+patterns drawn from N(0, 1), and NaN-filled pad rows.  It holds none of the attention
 arithmetic, so it can feed both the HIP path and the CPU oracle without
 coupling them.
 
-Buffers are flat ``uint16`` arrays of bf16 bit patterns (LSE: ``float32``).  A
+Buffers are flat ``uint16`` arrays of bf16 (default) or fp16 bit patterns
+(LSE: ``float32``).  A
 buffer layout gives, per tensor, the element strides between tokens and heads
 (the dim stride is always 1) and the row at which each sequence starts; the
 ragged offsets handed to the library are ``start_row * stride_t`` in elements.
@@ -39,7 +40,12 @@ CAUSAL_BOTTOM_RIGHT = 2
 
 BF16_PAD_NAN = 0x7FC0     # fills pad rows / gap columns of input buffers
 BF16_OUT_NAN = 0x7FC1     # pre-fill of bf16 output buffers (distinct payload)
+F16_PAD_NAN = 0x7E00      # the same two for fp16 buffers
+F16_OUT_NAN = 0x7E01
 F32_OUT_NAN = 0x7FC00011  # pre-fill of fp32 LSE buffers
+PAD_NAN = {"bf16": BF16_PAD_NAN, "f16": F16_PAD_NAN}
+OUT_NAN = {"bf16": BF16_OUT_NAN, "f16": F16_OUT_NAN}
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclass
@@ -89,18 +95,20 @@ def lse_layout(kind: str, rows: int, heads: int, start_rows) -> Layout:
     raise ValueError(kind)
 
 
-def _randn_bf16_bits(shape, gen: torch.Generator) -> np.ndarray:
+def _randn_bits(shape, gen: torch.Generator, dtype: str) -> np.ndarray:
+    """N(0, 1) in fp32, rounded to nearest even in `dtype`, as bit patterns."""
     x = torch.randn(*shape, generator=gen, dtype=torch.float32)
-    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x.to(TORCH_DTYPE[dtype]).view(torch.int16).numpy().view(np.uint16)
 
 
-def fill_buffer(layout: Layout, lengths: np.ndarray, gen: torch.Generator) -> np.ndarray:
-    """Flat bf16 buffer: N(0,1) in each sequence's valid rows, NaN elsewhere.
+def fill_buffer(layout: Layout, lengths: np.ndarray, gen: torch.Generator,
+                dtype: str = "bf16") -> np.ndarray:
+    """Flat bf16/fp16 buffer: N(0,1) in each sequence's valid rows, NaN elsewhere.
 
     Values are drawn for every physical row (so they depend on the seed and the
     buffer size only), then every element outside a valid row is NaN."""
-    vals = _randn_bf16_bits((layout.rows, layout.heads, layout.dim), gen)
-    flat = np.full(layout.span, BF16_PAD_NAN, dtype=np.uint16)
+    vals = _randn_bits((layout.rows, layout.heads, layout.dim), gen, dtype)
+    flat = np.full(layout.span, PAD_NAN[dtype], dtype=np.uint16)
     valid = valid_rows(layout, lengths)
     v = layout.view(flat)
     v[valid] = vals[valid]
@@ -118,8 +126,10 @@ def valid_rows(layout: Layout, lengths: np.ndarray) -> np.ndarray:
 
 
 def out_buffer(layout: Layout, kind: str = "bf16") -> np.ndarray:
-    if kind == "bf16":
-        return np.full(layout.span, BF16_OUT_NAN, dtype=np.uint16)
+    """An output buffer pre-filled with the NaN payload of its kind
+    ("bf16", "f16" or "f32")."""
+    if kind in OUT_NAN:
+        return np.full(layout.span, OUT_NAN[kind], dtype=np.uint16)
     return np.full(layout.span, F32_OUT_NAN, dtype=np.uint32).view(np.float32)
 
 
@@ -141,6 +151,7 @@ class Batch:
     layouts: dict = field(default_factory=dict)   # q k v o lse do dq dk dv
     data: dict = field(default_factory=dict)      # q k v do -> flat uint16
     window: np.ndarray | None = None  # int32 [3, 2] (left, right) per policy, -1 unbounded
+    dtype: str = "bf16"               # element type of Q, K, V, O, dO, dQ, dK, dV
 
     @property
     def batch(self) -> int:
@@ -168,7 +179,8 @@ def _with_gaps(lengths, gaps) -> np.ndarray:
 
 def build(name, seed, h_q, h_kv, dim, lq, lk, q_start, kv_start, *, default_policy,
           policy=None, q_causal_offset=None, lse_kind="token", scale=None,
-          q_rows=None, kv_rows=None, token_gaps=None, with_grad=True, window=None) -> Batch:
+          q_rows=None, kv_rows=None, token_gaps=None, with_grad=True, window=None,
+          dtype="bf16") -> Batch:
     """Assemble a batch from lengths and start rows.
 
     ``token_gaps`` maps tensor name -> n, giving that tensor a token stride of
@@ -191,14 +203,15 @@ def build(name, seed, h_q, h_kv, dim, lq, lk, q_start, kv_start, *, default_poli
               lq, lk, int(default_policy),
               None if policy is None else np.asarray(policy, np.int8),
               None if q_causal_offset is None else np.asarray(q_causal_offset, np.int32),
-              lay, {}, None if window is None else np.asarray(window, np.int32).reshape(3, 2))
+              lay, {}, None if window is None else np.asarray(window, np.int32).reshape(3, 2),
+              dtype)
     g = torch.Generator().manual_seed(seed)
-    b.data["q"] = fill_buffer(lay["q"], lq, g)
-    b.data["k"] = fill_buffer(lay["k"], lk, g)
-    b.data["v"] = fill_buffer(lay["v"], lk, g)
+    b.data["q"] = fill_buffer(lay["q"], lq, g, dtype)
+    b.data["k"] = fill_buffer(lay["k"], lk, g, dtype)
+    b.data["v"] = fill_buffer(lay["v"], lk, g, dtype)
     if with_grad:
         g2 = torch.Generator().manual_seed(seed + 100)
-        b.data["do"] = fill_buffer(lay["do"], lq, g2)
+        b.data["do"] = fill_buffer(lay["do"], lq, g2, dtype)
     return b
 
 
@@ -274,7 +287,7 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
                  policies=(PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT), per_seq_policy=True,
                  q_causal_offset: bool = False, lse_kind: str | None = None,
                  zero_lengths: bool = True, with_grad: bool = True,
-                 window=None) -> Batch:
+                 window=None, dtype: str = "bf16") -> Batch:
     """A small random ragged batch for parity tests: random lengths (some 0),
     random row gaps between sequences (separately for the query-side and
     key-side buffers), random per-tensor token-stride gaps n*H*D (n = 0..3),
@@ -308,7 +321,7 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
                  q_causal_offset=qco, lse_kind=lse_kind, token_gaps=gaps,
                  q_rows=int(q_start[-1]) + int(rng.integers(0, 8)),
                  kv_rows=int(kv_start[-1]) + int(rng.integers(0, 8)), with_grad=with_grad,
-                 window=window)
+                 window=window, dtype=dtype)
 
 
 def random_window(rng: np.random.Generator, max_size: int) -> np.ndarray:

@@ -11,7 +11,7 @@ import torch
 
 import variable_length_attention_ragged_amd as va
 
-from . import BF16_OUT_NAN, F32_OUT_NAN, Batch
+from . import F32_OUT_NAN, OUT_NAN, TORCH_DTYPE, Batch
 
 OUTPUTS = ("o", "lse", "dq", "dk", "dv")
 
@@ -32,7 +32,7 @@ class DeviceBatch:
         for n in ("q", "k", "v", "do"):
             if n in batch.data:
                 self.flat[n] = torch.from_numpy(batch.data[n].view(np.int16)).to(device) \
-                    .view(torch.bfloat16)
+                    .view(TORCH_DTYPE[batch.dtype])
         names = ("o", "lse") + (("dq", "dk", "dv") if with_grad else ())
         for n in names:
             self.flat[n] = self.fresh_output(n)
@@ -63,8 +63,8 @@ class DeviceBatch:
         if n == "lse":
             return torch.full((lay.span,), F32_OUT_NAN, dtype=torch.int32,
                               device=self.device).view(torch.float32)
-        return torch.full((lay.span,), BF16_OUT_NAN, dtype=torch.int16,
-                          device=self.device).view(torch.bfloat16)
+        return torch.full((lay.span,), OUT_NAN[self.batch.dtype], dtype=torch.int16,
+                          device=self.device).view(TORCH_DTYPE[self.batch.dtype])
 
     def rag(self, n: str) -> va.Ragged:
         lay = self.batch.layouts[n]
@@ -116,8 +116,8 @@ class DeviceBatch:
                                                    self.rag("dk"))
 
     def host(self, n: str) -> np.ndarray:
-        """Raw host copy: uint16 bit patterns for bf16 buffers, float32 for LSE."""
+        """Raw host copy: uint16 bit patterns for 16-bit buffers, float32 for LSE."""
         t = self.flat[n]
-        if t.dtype == torch.bfloat16:
+        if t.dtype in (torch.bfloat16, torch.float16):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
