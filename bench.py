@@ -36,6 +36,9 @@ WORKLOADS = {
                                          "packed causal lengths (seed 1002), H_q=H_kv=32, "
                                          "D=128, top-left causal, window (1024, 0), "
                                          "head-major LSE; fwd+bwd"),
+    "packed_causal_f16": ("config2_f16", "packed causal THD in fp16: the packed causal "
+                                         "lengths (seed 1002), H_q=H_kv=32, D=128, top-left "
+                                         "causal, head-major LSE; fwd+bwd"),
 }
 
 
@@ -146,8 +149,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="packed_causal",
-                    help="packed_causal (the headline configuration) or sliding_window "
-                         "(the same lengths with a causal window of 1024 keys back)")
+                    help="packed_causal (the headline configuration), sliding_window "
+                         "(the same lengths with a causal window of 1024 keys back) or "
+                         "packed_causal_f16 (the headline configuration in fp16)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times "
                          "(calibrates HBM byte counters against a known size) and exit")
@@ -247,7 +251,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": batch.dtype,
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.workload][1],

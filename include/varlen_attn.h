@@ -45,8 +45,11 @@
  * gap columns of strided views, rows of invalid sequences.  Those elements of
  * O, LSE, dQ, dK and dV keep their previous contents bit for bit.
  *
- * Data types: Q, K, V, O, dO, dQ, dK, dV are bf16 (stored as uint16 bit
- * patterns, round-to-nearest-even on output); LSE and the scale are fp32.
+ * Data types: Q, K, V, O, dO, dQ, dK, dV share one 16-bit element type, bf16
+ * or IEEE fp16 (TransformerEngine PR #3274, "Description": the per-sequence
+ * policy path supports FP16 and BF16 THD attention), stored as 16-bit
+ * patterns and rounded to nearest even on output; products accumulate in
+ * fp32.  LSE and the scale are fp32.
  */
 #ifndef VARLEN_ATTN_H
 #define VARLEN_ATTN_H
@@ -67,10 +70,10 @@ enum {
   VARLEN_ATTN_ERR_BATCH = 2,       /* batch < 0 */
   VARLEN_ATTN_ERR_HEAD_DIM = 3,    /* head_dim not 64 or 128 */
   VARLEN_ATTN_ERR_HEADS = 4,       /* h_q or h_kv < 1, or h_q % h_kv != 0 */
-  VARLEN_ATTN_ERR_ALIGN = 5,       /* bf16 data not 16-byte aligned, LSE not
+  VARLEN_ATTN_ERR_ALIGN = 5,       /* 16-bit data not 16-byte aligned, LSE not
                                       4-byte aligned, workspace not 256-byte
                                       aligned */
-  VARLEN_ATTN_ERR_STRIDE = 6,      /* bf16 strides not multiples of 8, or a
+  VARLEN_ATTN_ERR_STRIDE = 6,      /* 16-bit strides not multiples of 8, or a
                                       stride smaller than one row/head, or
                                       larger than the span */
   VARLEN_ATTN_ERR_SPAN = 7,        /* span_elems smaller than one row */
@@ -81,7 +84,14 @@ enum {
   VARLEN_ATTN_ERR_OFFSETS = 12,    /* a tensor gives both `ragged` and
                                       `ragged_scaled`, or ragged_multiplier is
                                       outside [1, 2^31) */
-  VARLEN_ATTN_ERR_WINDOW = 13      /* a window_size entry below -1 */
+  VARLEN_ATTN_ERR_WINDOW = 13,     /* a window_size entry below -1 */
+  VARLEN_ATTN_ERR_DTYPE = 14       /* dtype not VARLEN_ATTN_BF16 or _F16 */
+};
+
+/* Element types of the 16-bit tensors. */
+enum {
+  VARLEN_ATTN_BF16 = 0,
+  VARLEN_ATTN_F16 = 1
 };
 
 /* Mask policies (TransformerEngine names: padding, padding_causal,
@@ -99,7 +109,7 @@ enum {
  * outputs stay untouched) and its bits are ORed into *dev_status. */
 enum {
   VARLEN_ATTN_ST_NEG_LENGTH = 1,     /* Lq < 0 or Lk < 0 */
-  VARLEN_ATTN_ST_BAD_OFFSET = 2,     /* ragged[b] < 0, or a bf16 tensor's
+  VARLEN_ATTN_ST_BAD_OFFSET = 2,     /* ragged[b] < 0, or a 16-bit tensor's
                                         ragged[b] not a multiple of 8 */
   VARLEN_ATTN_ST_OUT_OF_SPAN = 4,    /* a row of the sequence would reach past
                                         span_elems */
@@ -146,7 +156,9 @@ typedef struct varlen_attn_tensor {
  * (then each causal policy uses its own alignment).  window_size: HOST int32
  * [6] = {left, right} for padding, top-left, bottom-right, each >= -1 (else
  * VARLEN_ATTN_ERR_WINDOW), read during the call only; NULL means no window
- * for any policy.  GQA: query head h reads key/value head h / (h_q / h_kv). */
+ * for any policy.  dtype: VARLEN_ATTN_BF16 (0) or VARLEN_ATTN_F16 (1), the
+ * element type of Q, K, V, O, dO, dQ, dK and dV.  GQA: query head h reads
+ * key/value head h / (h_q / h_kv). */
 typedef struct varlen_attn_problem {
   int32_t batch;
   int32_t h_q;
@@ -159,6 +171,7 @@ typedef struct varlen_attn_problem {
   int32_t default_policy;
   const int32_t* q_causal_offset;
   const int32_t* window_size;
+  int32_t dtype;
 } varlen_attn_problem;
 
 /* Byte offsets of the workspace regions (each 256-byte aligned) and the tile
@@ -230,7 +243,7 @@ int varlen_attn_bwd_workspace_size(const varlen_attn_problem* p, const varlen_at
 
 /* ---------------------------------------------------------------- compute */
 
-/* Forward.  Reads q, k, v (bf16); writes o (bf16) and lse (fp32) for the
+/* Forward.  Reads q, k, v (16-bit); writes o (16-bit) and lse (fp32) for the
  * valid rows of valid sequences only.  `workspace` (device, 256-byte aligned,
  * at least varlen_attn_fwd_workspace_size bytes) is overwritten.
  * `dev_status` (device int32, may be NULL) receives device status bits by
@@ -242,8 +255,8 @@ int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* o, const varlen_attn_tensor* lse, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream);
 
-/* Backward.  Reads q, k, v, o, dout (bf16) and lse (fp32, as written by the
- * forward); writes dq, dk, dv (bf16) for valid rows only.  dK and dV of key
+/* Backward.  Reads q, k, v, o, dout (16-bit) and lse (fp32, as written by the
+ * forward); writes dq, dk, dv (16-bit) for valid rows only.  dK and dV of key
  * rows bound by several consecutive sequences (identical K, V, dK and dV
  * offsets, e.g. context-parallel query chunks of one document) are the sums
  * over those sequences.  Other overlaps between the output rows of different
@@ -282,9 +295,9 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
  *   fwd_attention    O and LSE of every listed tile
  *   bwd_preprocess   -delta = -rowsum(dO * O) and lse_term (fp32, in the
  *                    workspace)
- *   bwd_dkdv         dK and dV (bf16), key-major: K/V resident, query tiles
+ *   bwd_dkdv         dK and dV (16-bit), key-major: K/V resident, query tiles
  *                    streamed
- *   bwd_dq           dQ (bf16), query-major: Q/dO resident, K/V tiles
+ *   bwd_dq           dQ (16-bit), query-major: Q/dO resident, K/V tiles
  *                    streamed */
 int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,

@@ -63,7 +63,7 @@ def _fwd(p, q=None, k=None, v=None, o=None, lse=None, ws=FAKE, ws_bytes=1 << 30)
     ("ws_align", B.ERR_ALIGN), ("ws_null", B.ERR_WORKSPACE),
     ("no_offsets", B.ERR_NULL), ("both_offsets", B.ERR_OFFSETS),
     ("multiplier0", B.ERR_OFFSETS), ("multiplier_big", B.ERR_OFFSETS),
-    ("window", B.ERR_WINDOW),
+    ("window", B.ERR_WINDOW), ("dtype", B.ERR_DTYPE),
 ])
 def test_host_validation_codes(case, code):
     p = _p()
@@ -104,6 +104,8 @@ def test_host_validation_codes(case, code):
         kw["v"] = _t(100 * 256, 256, 128, ragged=None, scaled=FAKE, mult=0)
     elif case == "multiplier_big":
         kw["o"] = _t(100 * 512, 512, 128, ragged=None, scaled=FAKE, mult=1 << 31)
+    elif case == "dtype":
+        p.dtype = 2
     elif case == "window":
         win = (ctypes.c_int32 * 6)(-1, -1, 128, 0, -1, -2)
         p.window_size = ctypes.addressof(win)

@@ -198,6 +198,49 @@ def test_window_with_aliased_kv_segments():
     check_backward(batch, dev)
 
 
+FP16 = [(s, d, w) for s, d, w in ((240, 64, None), (241, 128, None), (242, 128, "random"),
+                                   (243, 64, "random"), (244, 128, "random"))]
+
+
+@pytest.mark.parametrize("seed,dim,window", FP16)
+def test_fp16_random_fwd_bwd(seed, dim, window):
+    """IEEE fp16 inputs and outputs (fp16 MFMAs, P and dS packed as fp16)."""
+    batch = workloads.random_batch(seed, batch=6, max_len=400, h_q=4, h_kv=2, dim=dim,
+                                   q_causal_offset=(seed % 2 == 0), window=window, dtype="f16")
+    say(f"[fp16] seed={seed} D={dim} window={window if window is None else batch.window.tolist()}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
+def test_fp16_full_size_sampled():
+    """The packed causal workload's shape in fp16: sampled forward rows and the
+    gradients of one kv head."""
+    b16 = workloads.config2(with_grad=True)
+    batch = workloads.build("packed_causal_f16", 1102, 32, 32, 128, b16.lq, b16.lk,
+                            b16.layouts["q"].start_rows, b16.layouts["k"].start_rows,
+                            default_policy=workloads.CAUSAL_TOP_LEFT, lse_kind="head",
+                            dtype="f16")
+    say(f"[fp16 full] tokens={int(batch.lq.sum())}")
+    dev = _dev(batch, with_grad=True)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    assert int(dev.status.item()) == 0
+    _check_sampled_fwd(batch, dev, seed=16)
+    ref = oracle_bwd(batch, kv_heads=[21])
+    for n in ("dq", "dk", "dv"):
+        w = ref[n + "_written"]
+        g = oracle.bits_to_f64(dev.host(n)[w], batch.dtype)
+        err = np.abs(g - ref[n][w]).max()
+        say(f"  {n}: max abs err {err:.3e} over {int(w.sum())} elements")
+        assert err <= GRAD_TOL
+    _check_pads_untouched(batch, dev, ("o", "lse", "dq", "dk", "dv"))
+
+
 def test_many_tiny_sequences_fwd_bwd():
     """1100 sequences of 0..12 rows: almost every tile is a ragged tail, and the
     setup ranks more sequences than it keeps in LDS."""

@@ -75,6 +75,9 @@ class Ragged:
             self.multiplier if self.scaled is not None else 0)
 
 
+_DTYPES = {torch.bfloat16: _b.BF16, torch.float16: _b.F16}
+
+
 @dataclass
 class Problem:
     """Lengths, heads and mask policy (see include/varlen_attn.h)."""
@@ -91,6 +94,7 @@ class Problem:
     # (left, right) per policy in the order padding, top-left, bottom-right;
     # -1 unbounded.  Host values (six ints, flat or 3 x 2).
     window_size: object | None = None
+    dtype: torch.dtype = torch.bfloat16   # of Q, K, V, O, dO, dQ, dK, dV (bf16 or fp16)
 
     def c(self) -> varlen_attn_problem:
         def ptr(t):
@@ -104,11 +108,14 @@ class Problem:
             if len(vals) != 6:
                 raise ValueError("window_size needs (left, right) for each of the 3 policies")
             win = (ctypes.c_int32 * 6)(*vals)
+        if self.dtype not in _DTYPES:
+            raise TypeError("dtype must be torch.bfloat16 or torch.float16")
         prob = varlen_attn_problem(batch, self.h_q, self.h_kv, self.head_dim, scale,
                                    ptr(self.cu_seqlens_q), ptr(self.cu_seqlens_kv),
                                    ptr(self.mask_policy), self.default_policy,
                                    ptr(self.q_causal_offset),
-                                   None if win is None else ctypes.addressof(win))
+                                   None if win is None else ctypes.addressof(win),
+                                   _DTYPES[self.dtype])
         prob._window_keepalive = win  # the library reads it during the call
         return prob
 
@@ -158,7 +165,17 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def _check_dtypes(p, halves, lse):
+    """The 16-bit tensors must have the problem's element type, LSE fp32."""
+    for r in halves:
+        if r.view.dtype != p.dtype:
+            raise TypeError(f"tensor dtype {r.view.dtype} differs from the problem's {p.dtype}")
+    if lse.view.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+
+
 def _fwd_call(name, p, q, k, v, o, lse, workspace, dev_status, stream):
+    _check_dtypes(p, (q, k, v, o), lse)
     if workspace is None:
         workspace = _workspace(varlen_attn_fwd_workspace_size(p, o), o.view.device)
     code = getattr(lib(), name)(
@@ -186,6 +203,7 @@ def varlen_attn_fwd_setup(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged
 
 
 def _bwd_call(name, p, q, k, v, o, dout, lse, dq, dk, dv, workspace, dev_status, stream):
+    _check_dtypes(p, (q, k, v, o, dout, dq, dk, dv), lse)
     if workspace is None:
         workspace = _workspace(varlen_attn_bwd_workspace_size(p, lse, dq, dk), dq.view.device)
     code = getattr(lib(), name)(

@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(HERE, "libvarlen_attn.so")
 OK = 0
 ERR_NULL, ERR_BATCH, ERR_HEAD_DIM, ERR_HEADS, ERR_ALIGN, ERR_STRIDE = 1, 2, 3, 4, 5, 6
 ERR_SPAN, ERR_WORKSPACE, ERR_POLICY, ERR_SCALE, ERR_HIP = 7, 8, 9, 10, 11
-ERR_OFFSETS, ERR_WINDOW = 12, 13
+ERR_OFFSETS, ERR_WINDOW, ERR_DTYPE = 12, 13, 14
+# element types of the 16-bit tensors
+BF16, F16 = 0, 1
 # mask policies
 PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 # device status bits
@@ -35,7 +37,7 @@ class varlen_attn_problem(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("h_q", c_int32), ("h_kv", c_int32), ("head_dim", c_int32),
                 ("scale", c_float), ("cu_seqlens_q", c_void_p), ("cu_seqlens_kv", c_void_p),
                 ("mask_policy", c_void_p), ("default_policy", c_int32),
-                ("q_causal_offset", c_void_p), ("window_size", c_void_p)]
+                ("q_causal_offset", c_void_p), ("window_size", c_void_p), ("dtype", c_int32)]
 
 
 class varlen_attn_layout(ctypes.Structure):

@@ -81,6 +81,7 @@ int check_problem(const varlen_attn_problem* p) {
   if (p->window_size)
     for (int i = 0; i < 6; ++i)
       if (p->window_size[i] < -1) return VARLEN_ATTN_ERR_WINDOW;
+  if (p->dtype != VARLEN_ATTN_BF16 && p->dtype != VARLEN_ATTN_F16) return VARLEN_ATTN_ERR_DTYPE;
   return VARLEN_ATTN_OK;
 }
 
@@ -266,7 +267,7 @@ int run_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   f.group = p->h_q / p->h_kv;
   f.scale_log2 = p->scale * kLog2eHost;
   f.ws = s.ws;
-  if (launch_fwd(f, p->head_dim, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
+  if (launch_fwd(f, p->head_dim, p->dtype, st) != hipSuccess) return VARLEN_ATTN_ERR_HIP;
   return VARLEN_ATTN_OK;
 }
 
@@ -342,11 +343,11 @@ int run_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   a.scale = p->scale;
   a.scale_log2 = p->scale * kLog2eHost;
   a.ws = s.ws;
-  if ((stages & STAGE_BWD_PRE) && launch_bwd_pre(a, p->head_dim, st) != hipSuccess)
+  if ((stages & STAGE_BWD_PRE) && launch_bwd_pre(a, p->head_dim, p->dtype, st) != hipSuccess)
     return VARLEN_ATTN_ERR_HIP;
-  if ((stages & STAGE_BWD_DKDV) && launch_bwd_dkdv(a, p->head_dim, st) != hipSuccess)
+  if ((stages & STAGE_BWD_DKDV) && launch_bwd_dkdv(a, p->head_dim, p->dtype, st) != hipSuccess)
     return VARLEN_ATTN_ERR_HIP;
-  if ((stages & STAGE_BWD_DQ) && launch_bwd_dq(a, p->head_dim, st) != hipSuccess)
+  if ((stages & STAGE_BWD_DQ) && launch_bwd_dq(a, p->head_dim, p->dtype, st) != hipSuccess)
     return VARLEN_ATTN_ERR_HIP;
   return VARLEN_ATTN_OK;
 }
@@ -463,6 +464,7 @@ const char* varlen_attn_status_string(int code) {
     case VARLEN_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than the required size";
     case VARLEN_ATTN_ERR_POLICY: return "default_policy must be 0, 1 or 2";
     case VARLEN_ATTN_ERR_WINDOW: return "window_size entries must be >= -1";
+    case VARLEN_ATTN_ERR_DTYPE: return "dtype must be VARLEN_ATTN_BF16 or VARLEN_ATTN_F16";
     case VARLEN_ATTN_ERR_SCALE: return "scale must be finite";
     case VARLEN_ATTN_ERR_HIP: return "a HIP kernel launch failed";
     case VARLEN_ATTN_ERR_OFFSETS:

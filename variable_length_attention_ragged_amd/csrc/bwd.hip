@@ -36,8 +36,9 @@ constexpr int kThreads = 256;
 
 // ------------------------------------------------------------ preprocess
 
-template <int D>
+template <int D, class T>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
+  using V8 = vec8<T>;
   constexpr int LPR = D / 8;           // lanes per row, 8 elements each
   constexpr int RPP = 64 / LPR;        // rows per wave pass
   const WsView& w = a.ws;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
       const int64_t i = (int64_t)t * kFwdBlockM + r;
       const u32x4 ov = load16(a.o + obase + i * a.o_st + (int64_t)h * a.o_sh + 8 * li);
       const u32x4 dv = load16(a.dout + dobase + i * a.do_st + (int64_t)h * a.do_sh + 8 * li);
-      const bf16x8 o8 = as_bf16x8(ov), d8 = as_bf16x8(dv);
+      const V8 o8 = as_v8<T>(ov), d8 = as_v8<T>(dv);
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
@@ -90,8 +91,9 @@ struct QPos {
   bool done;
 };
 
-template <int D>
+template <int D, class T>
 __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t* entry, int g) {
+  using V8 = vec8<T>;
   constexpr int BM = kBwdBlockM, BN = kBwdBlockN;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int QB = BM / 32;  // 32-row query blocks per tile
@@ -113,7 +115,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
 
   // K/V fragments (B operands): lane holds key my_key, dims 16ks + 8hf .. +7.
   // A negative scale is folded into K for the score product only.
-  bf16x8 kf[KS], vf[KS];
+  V8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
@@ -121,8 +123,8 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
       kv = load16(a.k + kbase + (int64_t)my_key * a.k_st + (int64_t)g * a.k_sh + 16 * ks + 8 * hf);
       vv = load16(a.v + vbase + (int64_t)my_key * a.v_st + (int64_t)g * a.v_sh + 16 * ks + 8 * hf);
     }
-    kf[ks] = as_bf16x8(kv ^ flip);
-    vf[ks] = as_bf16x8(vv);
+    kf[ks] = as_v8<T>(kv ^ flip);
+    vf[ks] = as_v8<T>(vv);
   }
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -251,18 +253,18 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
     // (n/DB)%2, db = n%DB.
     constexpr int NN = QB * KS, NT = QB * 2 * DB;
     static_assert(QB == 2, "four-phase schedule");
-    bf16x8 na[3], nb[3];  // Q, dO fragments of natural steps, ring of 3
-    bf16x8 ta[3], tb[3];  // dO, Q fragments of transposed steps, ring of 3
+    V8 na[3], nb[3];  // Q, dO fragments of natural steps, ring of 3
+    V8 ta[3], tb[3];  // dO, Q fragments of transposed steps, ring of 3
     auto ld_nat = [&](int i) {
       const int qb = i / KS, ks = i % KS;
-      na[i % 3] = as_bf16x8(load16(qt + qoff[ks] + qb * 32 * D));
-      nb[i % 3] = as_bf16x8(load16(dt + qoff[ks] + qb * 32 * D));
+      na[i % 3] = as_v8<T>(load16(qt + qoff[ks] + qb * 32 * D));
+      nb[i % 3] = as_v8<T>(load16(dt + qoff[ks] + qb * 32 * D));
     };
     auto ld_tr = [&](int n) {
       const int kst = n / DB, db = n % DB;  // kst: 16-row step = 2*qb + st
       const int off = 16 * kst * D;
-      ta[n % 3] = concat_bf16(lds_read_tr(dt + tlo[db] + off), lds_read_tr(dt + thi[db] + off));
-      tb[n % 3] = concat_bf16(lds_read_tr(qt + tlo[db] + off), lds_read_tr(qt + thi[db] + off));
+      ta[n % 3] = concat8<T>(lds_read_tr(dt + tlo[db] + off), lds_read_tr(dt + thi[db] + off));
+      tb[n % 3] = concat8<T>(lds_read_tr(qt + tlo[db] + off), lds_read_tr(qt + thi[db] + off));
     };
     // Load for global step g of the combined stream (natural, then transposed).
     auto ld = [&](int g) {
@@ -270,7 +272,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
       else if (g < NN + NT) ld_tr(g - NN);
     };
 
-    bf16x8 pf[QB][2], dsf[QB][2];
+    V8 pf[QB][2], dsf[QB][2];
     float pe[QB][8], de[QB][8];
     // P and dS of entries 2k, 2k+1 of block qb; packs after every 4th chunk.
     auto softmax2 = [&](int qb, int k) {
@@ -283,9 +285,9 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
       }
       if ((k & 3) == 3) {
         const int st = k >> 2;
-        pf[qb][st] = pack_bf16x8(pe[qb][0], pe[qb][1], pe[qb][2], pe[qb][3], pe[qb][4],
+        pf[qb][st] = pack8<T>(pe[qb][0], pe[qb][1], pe[qb][2], pe[qb][3], pe[qb][4],
                                  pe[qb][5], pe[qb][6], pe[qb][7]);
-        dsf[qb][st] = pack_bf16x8(de[qb][0], de[qb][1], de[qb][2], de[qb][3], de[qb][4],
+        dsf[qb][st] = pack8<T>(de[qb][0], de[qb][1], de[qb][2], de[qb][3], de[qb][4],
                                   de[qb][5], de[qb][6], de[qb][7]);
       }
     };
@@ -363,13 +365,13 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
       if (key < lmax) {
         const int d = db * 32 + l32;
         a.dk[dkbase + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + d] =
-            to_bf16_bits(dk[db][r] * a.scale);
-        a.dv[dvbase + (int64_t)key * a.dv_st + (int64_t)g * a.dv_sh + d] = to_bf16_bits(dv[db][r]);
+            to_bits<T>(dk[db][r] * a.scale);
+        a.dv[dvbase + (int64_t)key * a.dv_st + (int64_t)g * a.dv_sh + d] = to_bits<T>(dv[db][r]);
       }
     }
 }
 
-template <int D>
+template <int D, class T>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t q0[kBwdBlockM * D], q1[kBwdBlockM * D];
   __shared__ __attribute__((aligned(16))) uint16_t d0[kBwdBlockM * D], d1[kBwdBlockM * D];
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
       if (j >= n_items) break;
       const int gi = j / n_tiles, tile = j - gi * n_tiles;
-      dkdv_item<D>(a, sm, w.bwd_tiles + 4 * tile, qq + kQueues * gi);
+      dkdv_item<D, T>(a, sm, w.bwd_tiles + 4 * tile, qq + kQueues * gi);
     }
   }
 }
@@ -406,8 +408,9 @@ struct DqSmem {
   uint16_t* v[2];
 };
 
-template <int D>
+template <int D, class T>
 __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int h, int g) {
+  using V8 = vec8<T>;
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16, DB = D / 32;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -450,7 +453,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q (sign folded as in the forward) and dO fragments: row i, dims 16ks + 8hf.
-  bf16x8 qf[KS], df[KS];
+  V8 qf[KS], df[KS];
   float s_init = 0.f, dl = 0.f;
   {
     const uint16_t* qrow = a.q + qbase + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * hf;
@@ -462,8 +465,8 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
         qv = load16(qrow + 16 * ks);
         dv = load16(drow + 16 * ks);
       }
-      qf[ks] = as_bf16x8(qv ^ flip);
-      df[ks] = as_bf16x8(dv);
+      qf[ks] = as_v8<T>(qv ^ flip);
+      df[ks] = as_v8<T>(dv);
     }
     if (row_ok) {
       const int64_t off = lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh;
@@ -519,7 +522,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     //      dS^T = P^T o (dP^T - delta).  The accumulators start at the row
     //      terms (-LSE*log2(e)/c and -delta).  Lane: query row i; entry r:
     //      key kb*32 + 8(r/4) + 4hf + r%4.
-    bf16x8 dsf[BN / 16];
+    V8 dsf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       f32x16 sc, dp;
@@ -529,14 +532,14 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
         dp[r] = dl;
       }
       {
-        bf16x8 ka[2], va[2];
-        ka[0] = as_bf16x8(load16(kt + koff[0] + kb * 32 * D));
-        va[0] = as_bf16x8(load16(vt + koff[0] + kb * 32 * D));
+        V8 ka[2], va[2];
+        ka[0] = as_v8<T>(load16(kt + koff[0] + kb * 32 * D));
+        va[0] = as_v8<T>(load16(vt + koff[0] + kb * 32 * D));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + 1 < KS) {
-            ka[(ks + 1) & 1] = as_bf16x8(load16(kt + koff[ks + 1] + kb * 32 * D));
-            va[(ks + 1) & 1] = as_bf16x8(load16(vt + koff[ks + 1] + kb * 32 * D));
+            ka[(ks + 1) & 1] = as_v8<T>(load16(kt + koff[ks + 1] + kb * 32 * D));
+            va[(ks + 1) & 1] = as_v8<T>(load16(vt + koff[ks + 1] + kb * 32 * D));
           }
           sc = mfma32(ka[ks & 1], qf[ks], sc);
           dp = mfma32(va[ks & 1], df[ks], dp);
@@ -557,7 +560,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int o = 8 * st;
-        dsf[kb * 2 + st] = pack_bf16x8(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4],
+        dsf[kb * 2 + st] = pack8<T>(dp[o], dp[o + 1], dp[o + 2], dp[o + 3], dp[o + 4],
                                        dp[o + 5], dp[o + 6], dp[o + 7]);
       }
     }
@@ -566,10 +569,10 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
 #pragma unroll
     for (int kst = 0; kst < BN / 16; ++kst) {
       const int base = ((kst >> 1) * 32 + 16 * (kst & 1)) * D;
-      bf16x8 kfr[DB];
+      V8 kfr[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        kfr[db] = concat_bf16(lds_read_tr(kt + klo[db] + base), lds_read_tr(kt + khi[db] + base));
+        kfr[db] = concat8<T>(lds_read_tr(kt + klo[db] + base), lds_read_tr(kt + khi[db] + base));
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] = mfma32(kfr[db], dsf[kst], acc[db]);
     }
@@ -589,14 +592,14 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
       for (int rr = 0; rr < 4; ++rr) {
         const int d = db * 32 + 8 * rr + 4 * hf;
         u32x2 pk;
-        pk[0] = pack_bf16x2(acc[db][4 * rr] * a.scale, acc[db][4 * rr + 1] * a.scale);
-        pk[1] = pack_bf16x2(acc[db][4 * rr + 2] * a.scale, acc[db][4 * rr + 3] * a.scale);
+        pk[0] = pack2<T>(acc[db][4 * rr] * a.scale, acc[db][4 * rr + 1] * a.scale);
+        pk[1] = pack2<T>(acc[db][4 * rr + 2] * a.scale, acc[db][4 * rr + 3] * a.scale);
         *(u32x2*)(qrow + d) = pk;
       }
   }
 }
 
-template <int D>
+template <int D, class T>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
@@ -621,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       const int gi = j / per_g, rem = j - gi * per_g;
       const int tile = rem / group, hh = rem - tile * group;
       const int g = qq + kQueues * gi;
-      dq_tile<D>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
+      dq_tile<D, T>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
     }
   }
 }
@@ -630,33 +633,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 constexpr int kFlatGrid = 4096;
 
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+template <int D, class T>
+void launch_pre_t(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
+}
+template <int D, class T>
+void launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {
+  const int g = persistent_grid((const void*)bwd_dkdv_kernel<D, T>, kThreads, 0);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(g), dim3(kThreads), 0, stream, a);
+}
+template <int D, class T>
+void launch_dq_t(const BwdArgs& a, hipStream_t stream) {
+  const int g = persistent_grid((const void*)bwd_dq_kernel<D, T>, kThreads, 0);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(g), dim3(kThreads), 0, stream, a);
+}
+
+// One of the four (head_dim, element type) instantiations of launcher L.
+#define VATTN_DISPATCH(L, a, head_dim, dtype, stream)                            \
+  do {                                                                           \
+    if ((dtype) == VARLEN_ATTN_F16) {                                            \
+      if ((head_dim) == 64) L<64, _Float16>(a, stream); else L<128, _Float16>(a, stream); \
+    } else {                                                                     \
+      if ((head_dim) == 64) L<64, __bf16>(a, stream); else L<128, __bf16>(a, stream);     \
+    }                                                                            \
+  } while (0)
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  VATTN_DISPATCH(launch_pre_t, a, head_dim, dtype, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 64) {
-    const int g = persistent_grid((const void*)bwd_dkdv_kernel<64>, kThreads, 0);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(g), dim3(kThreads), 0, stream, a);
-  } else {
-    const int g = persistent_grid((const void*)bwd_dkdv_kernel<128>, kThreads, 0);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(g), dim3(kThreads), 0, stream, a);
-  }
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  VATTN_DISPATCH(launch_dkdv_t, a, head_dim, dtype, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 64) {
-    const int g = persistent_grid((const void*)bwd_dq_kernel<64>, kThreads, 0);
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(g), dim3(kThreads), 0, stream, a);
-  } else {
-    const int g = persistent_grid((const void*)bwd_dq_kernel<128>, kThreads, 0);
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(g), dim3(kThreads), 0, stream, a);
-  }
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  VATTN_DISPATCH(launch_dq_t, a, head_dim, dtype, stream);
   return hipGetLastError();
 }
 

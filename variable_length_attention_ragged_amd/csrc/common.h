@@ -117,10 +117,12 @@ struct BwdArgs {
 
 // Kernel launchers (each enqueues on `stream` and returns the launch status).
 hipError_t launch_setup(const SetupArgs& a, hipStream_t stream);
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t stream);
+// `dtype`: VARLEN_ATTN_BF16 or VARLEN_ATTN_F16, the element type of the
+// 16-bit tensors.
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
 
 // Which kernels a call enqueues.
 enum Stage : unsigned {

@@ -42,8 +42,9 @@ struct FwdSmem {
   uint16_t* v[2];
 };
 
-template <int D>
+template <int D, class T>
 __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, int h, int g) {
+  using V8 = vec8<T>;
   constexpr int BM = kFwdBlockM, BN = kFwdBlockN;
   constexpr int KS = D / 16;   // MFMA k-steps over head_dim
   constexpr int DB = D / 32;   // 32-wide blocks of head_dim
@@ -95,7 +96,7 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q fragments (B operand of S^T): lane holds row i, dims 16ks + 8hf .. +7.
-  bf16x8 qf[KS];
+  V8 qf[KS];
   {
     const uint16_t* qrow = a.q + qbase + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * hf;
 #pragma unroll
@@ -103,7 +104,7 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
       u32x4 v = {0, 0, 0, 0};
       if (row_ok) v = load16(qrow + 16 * ks);
       v ^= flip;
-      qf[ks] = as_bf16x8(v);
+      qf[ks] = as_v8<T>(v);
     }
   }
 
@@ -162,16 +163,16 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     {
-      bf16x8 kfr[2][BN / 32];
+      V8 kfr[2][BN / 32];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
-        kfr[0][kb] = as_bf16x8(load16(kt + koff[0] + kb * 32 * D));
+        kfr[0][kb] = as_v8<T>(load16(kt + koff[0] + kb * 32 * D));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
 #pragma unroll
           for (int kb = 0; kb < BN / 32; ++kb)
-            kfr[(ks + 1) & 1][kb] = as_bf16x8(load16(kt + koff[ks + 1] + kb * 32 * D));
+            kfr[(ks + 1) & 1][kb] = as_v8<T>(load16(kt + koff[ks + 1] + kb * 32 * D));
         }
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) s[kb] = mfma32(kfr[ks & 1][kb], qf[ks], s[kb]);
@@ -220,7 +221,7 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
       m = m_new;
     }
     const float neg_m = (m == -INFINITY) ? 0.f : -m;
-    bf16x8 pf[BN / 16];
+    V8 pf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -233,18 +234,18 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
         }
         // entries 8st..8st+7 of block kb are keys
         // kb*32 + 16st + {4hf..4hf+3, 8+4hf..8+4hf+3}
-        pf[kb * 2 + st] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        pf[kb * 2 + st] = pack8<T>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       }
 
     // ---- O^T += V^T P^T: V read transposed in P's key order, one 16-key
     //      step ahead; DB independent accumulator chains.
     {
-      bf16x8 vfr[2][DB];
-      auto read_v = [&](int kst, bf16x8* out) {
+      V8 vfr[2][DB];
+      auto read_v = [&](int kst, V8* out) {
         const int base = ((kst >> 1) * 32 + 16 * (kst & 1)) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          out[db] = concat_bf16(lds_read_tr(vt + vlo[db] + base), lds_read_tr(vt + vhi[db] + base));
+          out[db] = concat8<T>(lds_read_tr(vt + vlo[db] + base), lds_read_tr(vt + vhi[db] + base));
       };
       read_v(0, vfr[0]);
 #pragma unroll
@@ -273,8 +274,8 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
       for (int rr = 0; rr < 4; ++rr) {
         const int d = db * 32 + 8 * rr + 4 * hf;
         u32x2 pk;
-        pk[0] = pack_bf16x2(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
-        pk[1] = pack_bf16x2(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
+        pk[0] = pack2<T>(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
+        pk[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
         *(u32x2*)(orow + d) = pk;
       }
     if (hf == 0) {
@@ -284,7 +285,7 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   }
 }
 
-template <int D>
+template <int D, class T>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
@@ -309,21 +310,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       const int gi = j / per_g, rem = j - gi * per_g;
       const int tile = rem / group, hh = rem - tile * group;
       const int g = qq + kQueues * gi;
-      fwd_tile<D>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
+      fwd_tile<D, T>(a, sm, ldm(w.fwd_tiles + (2 * tile)), ldm(w.fwd_tiles + (2 * tile + 1)), g * group + hh, g);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, hipStream_t stream) {
-  const void* k = head_dim == 64 ? (const void*)fwd_kernel<64> : (const void*)fwd_kernel<128>;
-  const int grid = persistent_grid(k, kThreads, 0);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(fwd_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(fwd_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+template <int D, class T>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const int grid = persistent_grid((const void*)fwd_kernel<D, T>, kThreads, 0);
+  hipLaunchKernelGGL((fwd_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  if (dtype == VARLEN_ATTN_F16)
+    return head_dim == 64 ? launch_fwd_t<64, _Float16>(a, stream)
+                          : launch_fwd_t<128, _Float16>(a, stream);
+  return head_dim == 64 ? launch_fwd_t<64, __bf16>(a, stream) : launch_fwd_t<128, __bf16>(a, stream);
 }
 
 }  // namespace vattn

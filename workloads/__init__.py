@@ -244,6 +244,16 @@ def config2_window(seed: int = 1002, with_grad: bool = False, left: int = 1024) 
     return b
 
 
+def config2_f16(seed: int = 1002, with_grad: bool = False) -> Batch:
+    """The packed causal workload (same lengths and layout) in IEEE fp16."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(128, 4096, size=16, endpoint=True)
+    start = _prefix(lens)
+    return build("packed_causal_f16_h32_d128", seed, 32, 32, 128, lens, lens, start, start,
+                 default_policy=CAUSAL_TOP_LEFT, lse_kind="head", with_grad=with_grad,
+                 dtype="f16")
+
+
 def config3(seed: int = 1003, with_grad: bool = True) -> Batch:
     rng = np.random.default_rng(seed)
     lens = rng.integers(64, 2048, size=32, endpoint=True)

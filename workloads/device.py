@@ -55,7 +55,8 @@ class DeviceBatch:
             torch.from_numpy(batch.q_causal_offset).to(device)
         self.problem = va.Problem(self.cu_q, self.cu_kv, batch.h_q, batch.h_kv, batch.dim,
                                   batch.scale, self.policy, batch.default_policy, self.qco,
-                                  None if batch.window is None else batch.window.tolist())
+                                  None if batch.window is None else batch.window.tolist(),
+                                  TORCH_DTYPE[batch.dtype])
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
 
     def fresh_output(self, n: str) -> torch.Tensor:
