@@ -155,27 +155,32 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
     const uint16_t* kt = sm.k[buf];
     const uint16_t* vt = sm.v[buf];
 
-    // ---- S^T = K Q^T (BN keys x 32 queries); the two 32-key chains
-    //      alternate and step ks+1's K fragments are read during step ks.
+    // ---- S^T = K Q^T (BN keys x 32 queries).  K fragments go through a ring
+    //      of KR steps read KR-1 steps ahead, and scheduling barriers keep
+    //      that order: left to itself the compiler reuses one register quad
+    //      and waits for each read right before its MFMA.
     f32x16 s[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     {
-      V8 kfr[2][BN / 32];
+      constexpr int KR = 4;
+      V8 kfr[KR][BN / 32];
+      auto ldk = [&](int ks) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-        kfr[0][kb] = as_v8<T>(load16(kt + koff[0] + kb * 32 * D));
+        for (int kb = 0; kb < BN / 32; ++kb)
+          kfr[ks % KR][kb] = as_v8<T>(load16(kt + koff[ks] + kb * 32 * D));
+      };
+#pragma unroll
+      for (int ks = 0; ks < KR - 1; ++ks) ldk(ks);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
+        if (ks + KR - 1 < KS) ldk(ks + KR - 1);
 #pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
-            kfr[(ks + 1) & 1][kb] = as_v8<T>(load16(kt + koff[ks + 1] + kb * 32 * D));
-        }
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) s[kb] = mfma32(kfr[ks & 1][kb], qf[ks], s[kb]);
+        for (int kb = 0; kb < BN / 32; ++kb) s[kb] = mfma32(kfr[ks % KR][kb], qf[ks], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
