@@ -54,20 +54,37 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     const int64_t obase = ldm(w.base + (T_O * B + b)), dobase = ldm(w.base + (T_DO * B + b));
     const int64_t lbase = ldm(w.base + (T_LSE * B + b));
     const int r_end = min(kFwdBlockM, lq - t * kFwdBlockM);
-    for (int r = wave * RPP + lr; r < r_end; r += 4 * RPP) {
-      const int64_t i = (int64_t)t * kFwdBlockM + r;
-      const u32x4 ov = load16(a.o + obase + i * a.o_st + (int64_t)h * a.o_sh + 8 * li);
-      const u32x4 dv = load16(a.dout + dobase + i * a.do_st + (int64_t)h * a.do_sh + 8 * li);
-      const V8 o8 = as_v8<T>(ov), d8 = as_v8<T>(dv);
+    // All of a lane's rows of the tile are loaded before any is reduced, so
+    // each lane keeps NR loads of O and dO in flight.
+    constexpr int NR = kFwdBlockM / (4 * RPP);
+    u32x4 ov[NR], dv[NR];
+    float lv[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int r = wave * RPP + lr + k * 4 * RPP;
+      ov[k] = u32x4{0, 0, 0, 0};
+      dv[k] = u32x4{0, 0, 0, 0};
+      lv[k] = 0.f;
+      if (r < r_end) {
+        const int64_t i = (int64_t)t * kFwdBlockM + r;
+        ov[k] = load16(a.o + obase + i * a.o_st + (int64_t)h * a.o_sh + 8 * li);
+        dv[k] = load16(a.dout + dobase + i * a.do_st + (int64_t)h * a.do_sh + 8 * li);
+        if (li == 0) lv[k] = a.lse[lbase + i * a.lse_st + (int64_t)h * a.lse_sh];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int r = wave * RPP + lr + k * 4 * RPP;
+      const V8 o8 = as_v8<T>(ov[k]), d8 = as_v8<T>(dv[k]);
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (li == 0) {
-        const int64_t off = lbase + i * a.lse_st + (int64_t)h * a.lse_sh;
+      if (li == 0 && r < r_end) {
+        const int64_t off = lbase + ((int64_t)t * kFwdBlockM + r) * a.lse_st + (int64_t)h * a.lse_sh;
         w.delta[off] = -acc;
-        w.lse_term[off] = -a.lse[off] * kLog2e / c;
+        w.lse_term[off] = -lv[k] * kLog2e / c;
       }
     }
   }

@@ -45,21 +45,38 @@ __device__ int check_tensor(const DevTensor& t, int64_t base, int64_t rows) {
   return (rows - 1 > room / t.st) ? VARLEN_ATTN_ST_OUT_OF_SPAN : 0;
 }
 
-// Sum over the query tiles of max(1, number of key tiles the tile reaches):
-// from its first row's lower band edge to its last row's upper one.  Lengths
-// are below 2^31, so the divisions run in 32 bits.
+// Cost of query tile t: max(1, number of key tiles it reaches), from its
+// first row's lower band edge to its last row's upper one.  Lengths are
+// below 2^31, so the divisions run in 32 bits.
+__device__ inline uint32_t tile_cost(uint32_t t, int64_t lq, int64_t lk, int64_t hi, int64_t lo,
+                                     int bm, int bn) {
+  const int64_t row_end = min(lq, (int64_t)(t + 1) * bm);
+  const int64_t kv_end = min(max(row_end + hi, (int64_t)0), lk);
+  const int64_t kv_begin = min(max((int64_t)t * bm + lo, (int64_t)0), lk);
+  const uint32_t tiles = ((uint32_t)kv_end + (uint32_t)bn - 1) / (uint32_t)bn -
+                         (uint32_t)kv_begin / (uint32_t)bn;
+  return max(1u, tiles);
+}
+
+// Sum of the tile costs of a sequence, by one thread.
 __device__ int64_t sequence_cost(int64_t lq, int64_t lk, int64_t hi, int64_t lo, int bm,
                                  int bn) {
   int64_t cost = 0;
   const uint32_t n = (uint32_t)((lq + bm - 1) / bm);
-  for (uint32_t t = 0; t < n; ++t) {
-    const int64_t row_end = min(lq, (int64_t)(t + 1) * bm);
-    const int64_t kv_end = min(max(row_end + hi, (int64_t)0), lk);
-    const int64_t kv_begin = min(max((int64_t)t * bm + lo, (int64_t)0), lk);
-    const uint32_t tiles = ((uint32_t)kv_end + (uint32_t)bn - 1) / (uint32_t)bn -
-                           (uint32_t)kv_begin / (uint32_t)bn;
-    cost += max(1u, tiles);
-  }
+  for (uint32_t t = 0; t < n; ++t) cost += tile_cost(t, lq, lk, hi, lo, bm, bn);
+  return cost;
+}
+
+// The same sum by one whole wave (lanes take every 64th tile); every lane
+// returns the total.
+__device__ int64_t sequence_cost_wave(int64_t lq, int64_t lk, int64_t hi, int64_t lo, int bm,
+                                      int bn) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t n = (uint32_t)((lq + bm - 1) / bm);
+  int64_t cost = 0;
+  for (uint32_t t = lane; t < n; t += 64) cost += tile_cost(t, lq, lk, hi, lo, bm, bn);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cost += __shfl_xor(cost, off);
   return cost;
 }
 
@@ -106,6 +123,12 @@ __device__ int64_t block_exclusive_scan(int n, F value, int32_t* out) {
   return total;
 }
 
+// L: the batch fits kLdsSeq, and the per-sequence state every phase reads
+// back (lengths, flags, costs, orders, positions, kv-group tables) lives in
+// LDS instead of the workspace scratch, so the phases chain through LDS
+// rather than through dependent global-memory round trips.  The outputs are
+// written to the workspace either way.
+template <bool L>
 __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   const int tid = threadIdx.x;
   const int B = a.batch;
@@ -122,18 +145,30 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
 
   // Scratch (64 bytes per sequence): int64 cost_f[B], cost_b[B], gcost[B];
   // int32 order[B], pos[B], gfirst[B], gsize[B], glmax[B], gorder[B], gpos[B],
-  // gidx[B].
-  int64_t* cost_f = (int64_t*)w.scratch;
-  int64_t* cost_b = cost_f + B;
-  int64_t* gcost = cost_b + B;
-  int32_t* order = (int32_t*)(gcost + B);
-  int32_t* pos = order + B;
-  int32_t* gfirst = pos + B;
-  int32_t* gsize = gfirst + B;
-  int32_t* glmax = gsize + B;
-  int32_t* gorder = glmax + B;
-  int32_t* gpos = gorder + B;
-  int32_t* gidx = gpos + B;
+  // gidx[B], same[B] (K, V, dK, dV bases equal those of b-1).  In LDS when L,
+  // together with copies of lq, lk and flags.
+  constexpr int NL = L ? kLdsSeq : 1;
+  __shared__ int64_t s_cost[3][NL];
+  __shared__ int32_t s_idx[9][NL];
+  __shared__ int32_t s_meta[5][NL];  // lq, lk, flags, hi, lo
+  int64_t* const gscratch = (int64_t*)w.scratch;
+  int32_t* const iscratch = (int32_t*)(gscratch + 3 * (int64_t)B);
+  int64_t* cost_f = L ? s_cost[0] : gscratch;
+  int64_t* cost_b = L ? s_cost[1] : gscratch + B;
+  int64_t* gcost = L ? s_cost[2] : gscratch + 2 * (int64_t)B;
+  int32_t* order = L ? s_idx[0] : iscratch;
+  int32_t* pos = L ? s_idx[1] : iscratch + B;
+  int32_t* gfirst = L ? s_idx[2] : iscratch + 2 * (int64_t)B;
+  int32_t* gsize = L ? s_idx[3] : iscratch + 3 * (int64_t)B;
+  int32_t* glmax = L ? s_idx[4] : iscratch + 4 * (int64_t)B;
+  int32_t* gorder = L ? s_idx[5] : iscratch + 5 * (int64_t)B;
+  int32_t* gpos = L ? s_idx[6] : iscratch + 6 * (int64_t)B;
+  int32_t* gidx = L ? s_idx[7] : iscratch + 7 * (int64_t)B;
+  int32_t* same = L ? s_idx[8] : iscratch + 8 * (int64_t)B;
+  // lq, lk, flags as read back by the later phases
+  const int32_t* m_lq = L ? s_meta[0] : w.lq;
+  const int32_t* m_lk = L ? s_meta[1] : w.lk;
+  const int32_t* m_flags = L ? s_meta[2] : w.flags;
   __syncthreads();
 
   // ---- per-sequence metadata and validation
@@ -181,21 +216,51 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     w.hi[b] = (int32_t)hi;
     w.lo[b] = (int32_t)lo;
     w.flags[b] = (valid ? 1 : 0) | (st << 8);
+    if (L) {
+      s_meta[0][b] = (int32_t)lq;
+      s_meta[1][b] = (int32_t)lk;
+      s_meta[2][b] = (valid ? 1 : 0) | (st << 8);
+      s_meta[3][b] = (int32_t)hi;
+      s_meta[4][b] = (int32_t)lo;
+    }
     for (int id = 0; id < T_COUNT; ++id)
       w.base[(int64_t)id * B + b] = a.t[id].present ? offset_of(a.t[id], b) : 0;
-    cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, hi, lo, a.bm, a.bn) : 0;
-    cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, hi, lo, a.bm_b, a.bn_b) : 0;
+    // does b bind the K, V, dK and dV rows of b-1 (one kv group)?
+    bool same_kv = b > 0;
+    for (int id : {(int)T_K, (int)T_V, (int)T_DK, (int)T_DV})
+      if (same_kv && a.t[id].present) same_kv = offset_of(a.t[id], b) == offset_of(a.t[id], b - 1);
+    same[b] = same_kv ? 1 : 0;
+    if (!L) {
+      cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, hi, lo, a.bm, a.bn) : 0;
+      cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, hi, lo, a.bm_b, a.bn_b) : 0;
+    }
     if (st) atomicOr(&s_status, st);
     if (valid && lq > 0) atomicAdd(&s_listed, 1);
   }
   __syncthreads();
+  if (L) {
+    // costs, one wave per sequence (a long sequence has tens of tiles)
+    const int wave = tid >> 6;
+    for (int b = wave; b < B; b += kSetupThreads / 64) {
+      const int64_t lq = s_meta[0][b], lk = s_meta[1][b], hi = s_meta[3][b], lo = s_meta[4][b];
+      const bool valid = s_meta[2][b] & 1;
+      const int64_t cf = (valid && lq > 0) ? sequence_cost_wave(lq, lk, hi, lo, a.bm, a.bn) : 0;
+      const int64_t cb =
+          (valid && a.backward) ? sequence_cost_wave(lq, lk, hi, lo, a.bm_b, a.bn_b) : 0;
+      if ((tid & 63) == 0) {
+        cost_f[b] = cf;
+        cost_b[b] = cb;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- forward tile list: rank listed sequences by (cost desc, index asc).
   //      Sort key: the cost of a listed sequence, -1 for the others.
   __shared__ int64_t s_key[kLdsSeq];
   __shared__ int32_t s_first[kLdsSeq];
   const bool in_lds = B <= kLdsSeq;
-  auto listed = [&](int b) { return (w.flags[b] & 1) && w.lq[b] > 0; };
+  auto listed = [&](int b) { return (m_flags[b] & 1) && m_lq[b] > 0; };
   if (in_lds)
     for (int b = tid; b < B; b += kSetupThreads) s_key[b] = listed(b) ? cost_f[b] : -1;
   __syncthreads();
@@ -218,22 +283,14 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   const int n_listed = s_listed;
   const int bm = a.bm;
   const int64_t n_fwd = block_exclusive_scan(
-      n_listed, [&](int r) { return ceil_div64(w.lq[order[r]], bm); }, pos);
+      n_listed, [&](int r) { return ceil_div64(m_lq[order[r]], bm); }, pos);
 
   // ---- backward kv groups
   int64_t n_bwd = 0;
   int n_groups = 0;
   if (a.backward) {
-    auto member = [&](int b) { return (w.flags[b] & 1) && w.lk[b] > 0; };
-    auto same_kv = [&](int b0, int b1) {
-      return w.base[(int64_t)T_K * B + b0] == w.base[(int64_t)T_K * B + b1] &&
-             w.base[(int64_t)T_V * B + b0] == w.base[(int64_t)T_V * B + b1] &&
-             w.base[(int64_t)T_DK * B + b0] == w.base[(int64_t)T_DK * B + b1] &&
-             w.base[(int64_t)T_DV * B + b0] == w.base[(int64_t)T_DV * B + b1];
-    };
-    auto starts = [&](int b) {
-      return member(b) && !(b > 0 && member(b - 1) && same_kv(b - 1, b));
-    };
+    auto member = [&](int b) { return (m_flags[b] & 1) && m_lk[b] > 0; };
+    auto starts = [&](int b) { return member(b) && !(b > 0 && member(b - 1) && same[b]); };
     // group index of each group start = number of starts before it
     const int64_t total_starts =
         block_exclusive_scan(B, [&](int b) { return (int64_t)(starts(b) ? 1 : 0); }, gidx);
@@ -241,10 +298,10 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
       if (!starts(b)) continue;
       const int g = gidx[b];
       int n = 1;
-      int lmax = w.lk[b];
+      int lmax = m_lk[b];
       int64_t c = cost_b[b];
-      while (b + n < B && member(b + n) && same_kv(b, b + n)) {
-        lmax = max(lmax, w.lk[b + n]);
+      while (b + n < B && member(b + n) && same[b + n]) {
+        lmax = max(lmax, m_lk[b + n]);
         c += cost_b[b + n];
         ++n;
       }
@@ -288,7 +345,7 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   if (!overflow) {
     for (int r = tid; r < n_listed; r += kSetupThreads) {
       const int b = order[r];
-      const int nt = (int)ceil_div64(w.lq[b], bm);
+      const int nt = (int)ceil_div64(m_lq[b], bm);
       int32_t* dst = w.fwd_tiles + 2 * (int64_t)pos[r];
       for (int k = 0; k < nt; ++k) {
         dst[2 * k] = b;
@@ -325,7 +382,10 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
 }  // namespace
 
 hipError_t launch_setup(const SetupArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(setup_kernel, dim3(1), dim3(kSetupThreads), 0, stream, a);
+  if (a.batch <= kLdsSeq)
+    hipLaunchKernelGGL(setup_kernel<true>, dim3(1), dim3(kSetupThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(setup_kernel<false>, dim3(1), dim3(kSetupThreads), 0, stream, a);
   return hipGetLastError();
 }
 
