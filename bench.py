@@ -3,7 +3,7 @@
 One step = one pass of the whole hot path over the packed causal workload
 (16 sequences with lengths U[128, 4096], seed 1002, H_q = H_kv = 32, D = 128,
 top-left causal, head-major LSE): setup + forward (O, LSE), then setup +
-dO.O preprocess + dK/dV (with dQ accumulation) + dQ finalize.  Inputs are
+dQ (which also forms the dO.O row terms) + dK/dV.  Inputs are
 resident in HBM before the timed region; workspaces are preallocated.
 
 Prints one JSON line.  ``value`` is causal-aware TFLOP/s of the whole step:
@@ -195,10 +195,8 @@ def main(argv=None) -> int:
     stages = [("setup (fwd)", lambda: dev.fwd_setup(workspace=fwd_ws)),
               ("fwd_kernel", lambda: dev.fwd_stage("varlen_attn_fwd_attention", workspace=fwd_ws)),
               ("setup (bwd)", lambda: dev.bwd_setup(workspace=bwd_ws)),
-              ("bwd_pre_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_preprocess",
-                                                       workspace=bwd_ws)),
-              ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws)),
-              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq", workspace=bwd_ws))]
+              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq", workspace=bwd_ws)),
+              ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws))]
 
     def step(ev=None):
         for n, (_, run) in enumerate(stages):

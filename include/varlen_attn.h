@@ -291,26 +291,18 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
  * kernel, and reads what the matching *_setup call (same arguments, earlier
  * on the same stream, same workspace) wrote there.  The full calls are
  * exactly: varlen_attn_fwd = fwd_setup, fwd_attention;
- * varlen_attn_bwd = bwd_setup, bwd_preprocess, bwd_dkdv, bwd_dq.
+ * varlen_attn_bwd = bwd_setup, bwd_dq, bwd_dkdv.
  *   fwd_attention    O and LSE of every listed tile
- *   bwd_preprocess   -delta = -rowsum(dO * O) and lse_term (fp32, in the
- *                    workspace)
- *   bwd_dkdv         dK and dV (16-bit), key-major: K/V resident, query tiles
- *                    streamed
  *   bwd_dq           dQ (16-bit), query-major: Q/dO resident, K/V tiles
- *                    streamed */
+ *                    streamed; also writes the row terms -delta =
+ *                    -rowsum(dO * O) and lse_term (fp32, in the workspace)
+ *   bwd_dkdv         dK and dV (16-bit), key-major: K/V resident, query tiles
+ *                    streamed; reads the row terms, so it follows bwd_dq */
 int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                               const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
                               void* workspace, size_t workspace_bytes, int32_t* dev_status,
                               void* stream);
-int varlen_attn_bwd_preprocess(const varlen_attn_problem* p, const varlen_attn_tensor* q,
-                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,
-                               const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
-                               const varlen_attn_tensor* lse, const varlen_attn_tensor* dq,
-                               const varlen_attn_tensor* dk, const varlen_attn_tensor* dv,
-                               void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                               void* stream);
 int varlen_attn_bwd_dkdv(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                          const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                          const varlen_attn_tensor* o, const varlen_attn_tensor* dout,

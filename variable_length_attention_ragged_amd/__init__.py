@@ -23,7 +23,7 @@ from ._binding import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, PADDING, ST_BAD_OFF
 
 __all__ = [
     "Ragged", "Problem", "varlen_attn_fwd", "varlen_attn_bwd", "varlen_attn_fwd_setup",
-    "varlen_attn_bwd_setup", "varlen_attn_fwd_attention", "varlen_attn_bwd_preprocess",
+    "varlen_attn_bwd_setup", "varlen_attn_fwd_attention",
     "varlen_attn_bwd_dkdv", "varlen_attn_bwd_dq", "varlen_attn_fwd_workspace_layout",
     "varlen_attn_bwd_workspace_layout", "varlen_attn_fwd_workspace_size",
     "varlen_attn_bwd_workspace_size", "status_string", "view_span", "PADDING",
@@ -252,6 +252,5 @@ def _bwd_stage(name):
     return run
 
 
-varlen_attn_bwd_preprocess = _bwd_stage("varlen_attn_bwd_preprocess")
 varlen_attn_bwd_dkdv = _bwd_stage("varlen_attn_bwd_dkdv")
 varlen_attn_bwd_dq = _bwd_stage("varlen_attn_bwd_dq")

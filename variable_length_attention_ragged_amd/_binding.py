@@ -77,8 +77,6 @@ _SIGNATURES = {
                               c_void_p, c_void_p],
     "varlen_attn_fwd_attention": [_P, _T, _T, _T, _T, _T, c_void_p, c_size_t, c_void_p,
                                   c_void_p],
-    "varlen_attn_bwd_preprocess": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,
-                                   c_void_p, c_void_p],
     "varlen_attn_bwd_dkdv": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,
                              c_void_p, c_void_p],
     "varlen_attn_bwd_dq": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,

@@ -343,11 +343,10 @@ int run_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const var
   a.scale = p->scale;
   a.scale_log2 = p->scale * kLog2eHost;
   a.ws = s.ws;
-  if ((stages & STAGE_BWD_PRE) && launch_bwd_pre(a, p->head_dim, p->dtype, st) != hipSuccess)
+  // the dQ pass writes the row terms the dK/dV pass reads
+  if ((stages & STAGE_BWD_DQ) && launch_bwd_dq(a, p->head_dim, p->dtype, st) != hipSuccess)
     return VARLEN_ATTN_ERR_HIP;
   if ((stages & STAGE_BWD_DKDV) && launch_bwd_dkdv(a, p->head_dim, p->dtype, st) != hipSuccess)
-    return VARLEN_ATTN_ERR_HIP;
-  if ((stages & STAGE_BWD_DQ) && launch_bwd_dq(a, p->head_dim, p->dtype, st) != hipSuccess)
     return VARLEN_ATTN_ERR_HIP;
   return VARLEN_ATTN_OK;
 }
@@ -422,7 +421,7 @@ int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* dk, const varlen_attn_tensor* dv, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
   return run_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, dev_status,
-                 stream, STAGE_SETUP | STAGE_BWD_PRE | STAGE_BWD_DKDV | STAGE_BWD_DQ);
+                 stream, STAGE_SETUP | STAGE_BWD_DQ | STAGE_BWD_DKDV);
 }
 
 int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
@@ -447,7 +446,6 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
                    dev_status, stream, STAGE);                                                 \
   }
 
-VATTN_BWD_STAGE(varlen_attn_bwd_preprocess, STAGE_BWD_PRE)
 VATTN_BWD_STAGE(varlen_attn_bwd_dkdv, STAGE_BWD_DKDV)
 VATTN_BWD_STAGE(varlen_attn_bwd_dq, STAGE_BWD_DQ)
 

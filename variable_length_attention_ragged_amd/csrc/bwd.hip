@@ -1,11 +1,13 @@
-// Backward kernels: preprocess, dK/dV pass, dQ pass.
+// Backward kernels: dQ pass (with the row terms), then dK/dV pass.
 //
-//   preprocess   delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32), stored
-//                negated, and the score row term -LSE[i,h]*log2(e)/c.  Both
-//                live in the workspace with the element offsets of LSE, as the
-//                softmax row-sum intermediate of cudnn-frontend PR #462 ("Root
-//                cause") lives on its user tensor's strides, which is why the
-//                workspace is sized from LSE's full span.
+//   row terms    delta[i,h] = sum_d dO[i,h,d] * O[i,h,d] (fp32), stored
+//                negated, and the score row term -LSE[i,h]*log2(e)/c, formed
+//                by the dQ pass (which holds each row's dO anyway) and written
+//                for the dK/dV pass.  Both live in the workspace with the
+//                element offsets of LSE, as the softmax row-sum intermediate
+//                of cudnn-frontend PR #462 ("Root cause") lives on its user
+//                tensor's strides, which is why the workspace is sized from
+//                LSE's full span.
 //   dkdv         one item = (kv group, 128-key tile, kv head).  Each wave keeps
 //                32 keys of K and V in registers; 32-row query tiles of every
 //                query head of the GQA group and every member sequence of the
@@ -33,62 +35,6 @@ namespace vattn {
 namespace {
 
 constexpr int kThreads = 256;
-
-// ------------------------------------------------------------ preprocess
-
-template <int D, class T>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-  using V8 = vec8<T>;
-  constexpr int LPR = D / 8;           // lanes per row, 8 elements each
-  constexpr int RPP = 64 / LPR;        // rows per wave pass
-  const WsView& w = a.ws;
-  const int B = a.batch;
-  const int n_items = ldm(w.header + 0) * a.h_q;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane % LPR, lr = lane / LPR;
-  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int tile = item / a.h_q, h = item - tile * a.h_q;
-    const int b = ldm(w.fwd_tiles + (2 * tile)), t = ldm(w.fwd_tiles + (2 * tile + 1));
-    const int lq = ldm(w.lq + b);
-    const int64_t obase = ldm(w.base + (T_O * B + b)), dobase = ldm(w.base + (T_DO * B + b));
-    const int64_t lbase = ldm(w.base + (T_LSE * B + b));
-    const int r_end = min(kFwdBlockM, lq - t * kFwdBlockM);
-    // All of a lane's rows of the tile are loaded before any is reduced, so
-    // each lane keeps NR loads of O and dO in flight.
-    constexpr int NR = kFwdBlockM / (4 * RPP);
-    u32x4 ov[NR], dv[NR];
-    float lv[NR];
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int r = wave * RPP + lr + k * 4 * RPP;
-      ov[k] = u32x4{0, 0, 0, 0};
-      dv[k] = u32x4{0, 0, 0, 0};
-      lv[k] = 0.f;
-      if (r < r_end) {
-        const int64_t i = (int64_t)t * kFwdBlockM + r;
-        ov[k] = load16(a.o + obase + i * a.o_st + (int64_t)h * a.o_sh + 8 * li);
-        dv[k] = load16(a.dout + dobase + i * a.do_st + (int64_t)h * a.do_sh + 8 * li);
-        if (li == 0) lv[k] = a.lse[lbase + i * a.lse_st + (int64_t)h * a.lse_sh];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int r = wave * RPP + lr + k * 4 * RPP;
-      const V8 o8 = as_v8<T>(ov[k]), d8 = as_v8<T>(dv[k]);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (li == 0 && r < r_end) {
-        const int64_t off = lbase + ((int64_t)t * kFwdBlockM + r) * a.lse_st + (int64_t)h * a.lse_sh;
-        w.delta[off] = -acc;
-        w.lse_term[off] = -lv[k] * kLog2e / c;
-      }
-    }
-  }
-}
 
 // ------------------------------------------------------------ dK / dV
 
@@ -439,6 +385,7 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
   const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
   const int64_t hi = ldm(w.hi + b), lo = ldm(w.lo + b);  // band: i + lo <= key <= i + hi
   const int64_t qbase = ldm(w.base + (T_Q * B + b)), dobase = ldm(w.base + (T_DO * B + b));
+  const int64_t obase = ldm(w.base + (T_O * B + b));
   const int64_t kbase = ldm(w.base + (T_K * B + b)), vbase = ldm(w.base + (T_V * B + b));
   const int64_t lbase = ldm(w.base + (T_LSE * B + b)), dqbase = ldm(w.base + (T_DQ * B + b));
 
@@ -470,25 +417,43 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
   const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q (sign folded as in the forward) and dO fragments: row i, dims 16ks + 8hf.
+  // The row terms come from O, dO and LSE here, and are written for the dK/dV
+  // pass: -delta = -sum_d dO*O (each lane half sums its 64 dims), and the
+  // score row term -LSE*log2(e)/c.
   V8 qf[KS], df[KS];
   float s_init = 0.f, dl = 0.f;
   {
     const uint16_t* qrow = a.q + qbase + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * hf;
     const uint16_t* drow = a.dout + dobase + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + 8 * hf;
+    const uint16_t* orow = a.o + obase + (int64_t)i * a.o_st + (int64_t)h * a.o_sh + 8 * hf;
+    const int64_t off = lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh;
+    u32x4 ov[KS];
+    float lse = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 qv = {0, 0, 0, 0}, dv = {0, 0, 0, 0};
+      ov[ks] = u32x4{0, 0, 0, 0};
       if (row_ok) {
         qv = load16(qrow + 16 * ks);
         dv = load16(drow + 16 * ks);
+        ov[ks] = load16(orow + 16 * ks);
       }
       qf[ks] = as_v8<T>(qv ^ flip);
       df[ks] = as_v8<T>(dv);
     }
-    if (row_ok) {
-      const int64_t off = lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh;
-      s_init = w.lse_term[off];
-      dl = w.delta[off];
+    if (row_ok) lse = a.lse[off];
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V8 o8 = as_v8<T>(ov[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)df[ks][e];
+    }
+    dl = -pair_sum(acc);
+    s_init = -lse * kLog2e / c;
+    if (row_ok && hf == 0) {
+      w.delta[off] = dl;
+      w.lse_term[off] = s_init;
     }
   }
 
@@ -651,10 +616,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 constexpr int kFlatGrid = 4096;
 
 template <int D, class T>
-void launch_pre_t(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3(kFlatGrid), dim3(kThreads), 0, stream, a);
-}
-template <int D, class T>
 void launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {
   const int g = persistent_grid((const void*)bwd_dkdv_kernel<D, T>, kThreads, 0);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3(g), dim3(kThreads), 0, stream, a);
@@ -674,11 +635,6 @@ void launch_dq_t(const BwdArgs& a, hipStream_t stream) {
       if ((head_dim) == 64) L<64, __bf16>(a, stream); else L<128, __bf16>(a, stream);     \
     }                                                                            \
   } while (0)
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
-  VATTN_DISPATCH(launch_pre_t, a, head_dim, dtype, stream);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
   VATTN_DISPATCH(launch_dkdv_t, a, head_dim, dtype, stream);

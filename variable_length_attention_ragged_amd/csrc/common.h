@@ -120,7 +120,6 @@ hipError_t launch_setup(const SetupArgs& a, hipStream_t stream);
 // `dtype`: VARLEN_ATTN_BF16 or VARLEN_ATTN_F16, the element type of the
 // 16-bit tensors.
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, hipStream_t stream);
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
 
@@ -128,7 +127,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, hipStream_t 
 enum Stage : unsigned {
   STAGE_SETUP = 1u,
   STAGE_FWD = 2u,
-  STAGE_BWD_PRE = 4u,
   STAGE_BWD_DKDV = 8u,
   STAGE_BWD_DQ = 16u,
 };
