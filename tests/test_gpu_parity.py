@@ -417,6 +417,51 @@ def test_scaled_offset_multiplier_is_applied_on_device():
     compare_bf16(batch, "o", dev.host("o"), ref["o"], ref["o_written"], O_TOL)
 
 
+def test_graph_capture_replays_match_eager():
+    """The full forward and backward calls captured in one HIP graph (they
+    allocate nothing and never synchronise): three replays, each on new Q and
+    dO values written into the captured buffers, with eager work and a
+    synchronisation between replays, each bit-identical to an eager run on
+    the same inputs in separate buffers."""
+    batch = workloads.random_batch(700, batch=6, max_len=300, h_q=4, h_kv=2, dim=128,
+                                   window="random", q_causal_offset=True)
+    say(f"[graph] lq={batch.lq.tolist()} window={batch.window.tolist()}")
+    cap = _dev(batch)
+    fws = torch.empty(cap.fwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
+    bws = torch.empty(cap.bwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
+    cap.fwd(workspace=fws)  # warm-up outside the capture
+    cap.bwd(workspace=bws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap.fwd(workspace=fws)
+        cap.bwd(workspace=bws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(701)
+    for rep in range(3):
+        for n in ("q", "do"):
+            fresh = torch.randn(cap.flat[n].shape, generator=gen, device="cuda")
+            src = fresh.to(cap.flat[n].dtype)
+            valid = ~torch.isnan(cap.flat[n].float())   # keep the NaN pad rows
+            cap.flat[n].copy_(torch.where(valid, src, cap.flat[n]))
+        ref = _dev(batch)
+        for n in ("q", "do"):
+            ref.flat[n].copy_(cap.flat[n])
+        g.replay()
+        ref.fwd()  # eager work between replays, on its own buffers
+        ref.bwd()
+        torch.cuda.synchronize()
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            view = torch.int32 if n == "lse" else torch.int16
+            assert torch.equal(cap.flat[n].view(view), ref.flat[n].view(view)), (rep, n)
+        assert int(cap.status.item()) == int(ref.status.item()) == 0
+    # and the last replay matches the oracle
+    for n in ("q", "do"):
+        batch.data[n] = cap.flat[n].view(torch.int16).cpu().numpy().view(np.uint16)
+    check_forward(batch, cap)
+    check_backward(batch, cap)
+
+
 def test_workspace_guard_bands():
     batch = workloads.random_batch(600, batch=5, max_len=300, dim=128)
     dev = _dev(batch)
