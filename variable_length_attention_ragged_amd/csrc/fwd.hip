@@ -40,7 +40,12 @@ template <int D>
 struct FwdSmem {
   uint16_t* k[2];
   uint16_t* v[2];
+  uint16_t* stage;  // kStageElems per wave, for the output rows
 };
+
+// Output staging: 32 rows x 64 columns per wave, one 128-byte line per row.
+constexpr int kStageCols = 64;
+constexpr int kStageElems = 32 * kStageCols;
 
 template <int D, class T>
 __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, int h, int g) {
@@ -268,25 +273,55 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
     if (n + 1 < n_kv) step(std::integral_constant<int, 1>{}, n + 1);
   }
 
-  // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2.
+  // A lane holds 4-column pieces of one row, so stores straight from the
+  // accumulators would write 16 bytes into each of 32 rows per instruction.
+  // Each wave instead passes its 32 x D block through its own LDS area, 64
+  // columns at a time (XOR-swizzled like a 64-column tile), and stores whole
+  // 128-byte row segments, 16 bytes per lane.
   l = pair_sum(l);
-  if (row_ok) {
+  if (!wave_active) return;
+  {
+    uint16_t* stage = sm.stage + wave * kStageElems;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = a.o + obase + (int64_t)i * a.o_st + (int64_t)h * a.o_sh;
+    // Lane offsets are formed here from values the compiler cannot move
+    // (add_in_place): hoisted out of the item loop, they would hold
+    // registers through the whole key loop.
+    const int wsw = add_in_place(swz<kStageCols>(l32), 0);
+    const int wrow = l32 * kStageCols + 4 * hf;
+    constexpr int CPR = kStageCols / 8;   // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;         // rows per wave-wide store
+    const int c = add_in_place(lane % CPR, 0), rl = add_in_place(lane / CPR, 0);
+    uint16_t* obase_h = a.o + obase + (int64_t)h * a.o_sh;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int q = 0; q < D / kStageCols; ++q) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = db * 32 + 8 * rr + 4 * hf;
-        u32x2 pk;
-        pk[0] = pack2<T>(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
-        pk[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
-        *(u32x2*)(orow + d) = pk;
+      for (int db2 = 0; db2 < 2; ++db2)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int db = 2 * q + db2;
+          u32x2 pk;
+          pk[0] = pack2<T>(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
+          pk[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
+          *(u32x2*)(stage + wrow + (((db2 * 4 + rr) ^ wsw) << 3)) = pk;
+        }
+      // The rows are read back by other lanes of this wave.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += RPI) {
+        const int r = r0 + rl;
+        const u32x4 v = *(const u32x4*)(stage + r * kStageCols + ((c ^ swz<kStageCols>(r)) << 3));
+        if (wq0 + r < lq)
+          *(u32x4*)(obase_h + (int64_t)(wq0 + r) * a.o_st + q * kStageCols + 8 * c) = v;
       }
-    if (hf == 0) {
-      const float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-      a.lse[lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh] = lse;
     }
+    // Wave 0's area also holds the claimed item index: its next write must
+    // not be moved above these accesses.
+    asm volatile("" ::: "memory");
+  }
+  if (row_ok && hf == 0) {
+    const float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    a.lse[lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh] = lse;
   }
 }
 
@@ -294,8 +329,11 @@ template <int D, class T>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
-  __shared__ int s_item;
-  FwdSmem<D> sm{{k0, k1}, {v0, v1}};
+  // Output staging for the four waves.  The claimed item index lives in
+  // wave 0's area: thread 0 writes it only after its own wave's stores.
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4 * kStageElems];
+  int& s_item = *(int*)stg;
+  FwdSmem<D> sm{{k0, k1}, {v0, v1}, stg};
   const WsView& w = a.ws;
   const int n_tiles = ldm(w.header + 0);
   const int xcd = xcc_id() & (kQueues - 1);
