@@ -369,6 +369,7 @@ template <int D>
 struct DqSmem {
   uint16_t* k[2];
   uint16_t* v[2];
+  uint16_t* stage;  // kStageElems per wave, for the dQ rows
 };
 
 template <int D, class T>
@@ -566,27 +567,21 @@ __device__ void dq_tile(const BwdArgs& a, const DqSmem<D> sm, int b, int t, int 
     if (n + 1 < n_kv) step(std::integral_constant<int, 1>{}, n + 1);
   }
 
-  if (row_ok) {
-    uint16_t* qrow = a.dq + dqbase + (int64_t)i * a.dq_st + (int64_t)h * a.dq_sh;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d = db * 32 + 8 * rr + 4 * hf;
-        u32x2 pk;
-        pk[0] = pack2<T>(acc[db][4 * rr] * a.scale, acc[db][4 * rr + 1] * a.scale);
-        pk[1] = pack2<T>(acc[db][4 * rr + 2] * a.scale, acc[db][4 * rr + 3] * a.scale);
-        *(u32x2*)(qrow + d) = pk;
-      }
-  }
+  if (!wave_active) return;
+  store_rows_staged<D, T>(acc, a.scale, sm.stage + wave * kStageElems,
+                          a.dq + dqbase + (int64_t)wq0 * a.dq_st + (int64_t)h * a.dq_sh, a.dq_st,
+                          min(32, lq - wq0));
 }
 
 template <int D, class T>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k0[kFwdBlockN * D], k1[kFwdBlockN * D];
   __shared__ __attribute__((aligned(16))) uint16_t v0[kFwdBlockN * D], v1[kFwdBlockN * D];
-  __shared__ int s_item;
-  DqSmem<D> sm{{k0, k1}, {v0, v1}};
+  // dQ staging for the four waves.  The claimed item index lives in wave
+  // 0's area: thread 0 writes it only after its own wave's stores.
+  __shared__ __attribute__((aligned(16))) uint16_t stg[4 * kStageElems];
+  int& s_item = *(int*)stg;
+  DqSmem<D> sm{{k0, k1}, {v0, v1}, stg};
   const WsView& w = a.ws;
   const int n_tiles = ldm(w.header + 0);
   const int xcd = xcc_id() & (kQueues - 1);

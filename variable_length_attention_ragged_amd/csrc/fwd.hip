@@ -43,10 +43,6 @@ struct FwdSmem {
   uint16_t* stage;  // kStageElems per wave, for the output rows
 };
 
-// Output staging: 32 rows x 64 columns per wave, one 128-byte line per row.
-constexpr int kStageCols = 64;
-constexpr int kStageElems = 32 * kStageCols;
-
 template <int D, class T>
 __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, int h, int g) {
   using V8 = vec8<T>;
@@ -274,51 +270,11 @@ __device__ void fwd_tile(const FwdArgs& a, const FwdSmem<D> sm, int b, int t, in
   }
 
   // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2.
-  // A lane holds 4-column pieces of one row, so stores straight from the
-  // accumulators would write 16 bytes into each of 32 rows per instruction.
-  // Each wave instead passes its 32 x D block through its own LDS area, 64
-  // columns at a time (XOR-swizzled like a 64-column tile), and stores whole
-  // 128-byte row segments, 16 bytes per lane.
   l = pair_sum(l);
   if (!wave_active) return;
-  {
-    uint16_t* stage = sm.stage + wave * kStageElems;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    // Lane offsets are formed here from values the compiler cannot move
-    // (add_in_place): hoisted out of the item loop, they would hold
-    // registers through the whole key loop.
-    const int wsw = add_in_place(swz<kStageCols>(l32), 0);
-    const int wrow = l32 * kStageCols + 4 * hf;
-    constexpr int CPR = kStageCols / 8;   // 16-byte chunks per staged row
-    constexpr int RPI = 64 / CPR;         // rows per wave-wide store
-    const int c = add_in_place(lane % CPR, 0), rl = add_in_place(lane / CPR, 0);
-    uint16_t* obase_h = a.o + obase + (int64_t)h * a.o_sh;
-#pragma unroll
-    for (int q = 0; q < D / kStageCols; ++q) {
-#pragma unroll
-      for (int db2 = 0; db2 < 2; ++db2)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int db = 2 * q + db2;
-          u32x2 pk;
-          pk[0] = pack2<T>(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv);
-          pk[1] = pack2<T>(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv);
-          *(u32x2*)(stage + wrow + (((db2 * 4 + rr) ^ wsw) << 3)) = pk;
-        }
-      // The rows are read back by other lanes of this wave.
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int r0 = 0; r0 < 32; r0 += RPI) {
-        const int r = r0 + rl;
-        const u32x4 v = *(const u32x4*)(stage + r * kStageCols + ((c ^ swz<kStageCols>(r)) << 3));
-        if (wq0 + r < lq)
-          *(u32x4*)(obase_h + (int64_t)(wq0 + r) * a.o_st + q * kStageCols + 8 * c) = v;
-      }
-    }
-    // Wave 0's area also holds the claimed item index: its next write must
-    // not be moved above these accesses.
-    asm volatile("" ::: "memory");
-  }
+  store_rows_staged<D, T>(acc, l > 0.f ? 1.f / l : 0.f, sm.stage + wave * kStageElems,
+                          a.o + obase + (int64_t)wq0 * a.o_st + (int64_t)h * a.o_sh, a.o_st,
+                          min(32, lq - wq0));
   if (row_ok && hf == 0) {
     const float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     a.lse[lbase + (int64_t)i * a.lse_st + (int64_t)h * a.lse_sh] = lse;

@@ -98,6 +98,56 @@ struct TileLoad {
   }
 };
 
+// Output staging: 32 rows x 64 columns per wave, one 128-byte line per row.
+constexpr int kStageCols = 64;
+constexpr int kStageElems = 32 * kStageCols;
+
+// Stores one wave's 32 x D output block, held as MFMA accumulators (lane l
+// has row l % 32; acc[db][r] is column db*32 + 8(r/4) + 4(l/32) + r%4),
+// times `mul` as 16-bit values.  Straight from the accumulators every store
+// would write 16 bytes into each of 32 rows; the block goes instead through
+// the wave's kStageElems LDS area, 64 columns at a time (XOR-swizzled like
+// a 64-column tile), and leaves as whole 128-byte row segments, 16 bytes
+// per lane.  `out` is row 0 of the block, `st` the row stride (elements);
+// rows from `nrows` on are not written.
+template <int D, class T>
+__device__ __forceinline__ void store_rows_staged(const f32x16* acc, float mul, uint16_t* stage,
+                                                  uint16_t* out, int64_t st, int nrows) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+  // Lane offsets are formed here from values the compiler cannot move
+  // (add_in_place): hoisted out of a caller's item loop, they would hold
+  // registers through its whole key loop.
+  const int wsw = add_in_place(swz<kStageCols>(l32), 0);
+  const int wrow = l32 * kStageCols + 4 * hf;
+  constexpr int CPR = kStageCols / 8;  // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPR;        // rows per wave-wide store
+  const int c = add_in_place(lane % CPR, 0), rl = add_in_place(lane / CPR, 0);
+#pragma unroll
+  for (int q = 0; q < D / kStageCols; ++q) {
+#pragma unroll
+    for (int db2 = 0; db2 < 2; ++db2)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const f32x16& x = acc[2 * q + db2];
+        u32x2 pk;
+        pk[0] = pack2<T>(x[4 * rr] * mul, x[4 * rr + 1] * mul);
+        pk[1] = pack2<T>(x[4 * rr + 2] * mul, x[4 * rr + 3] * mul);
+        *(u32x2*)(stage + wrow + (((db2 * 4 + rr) ^ wsw) << 3)) = pk;
+      }
+    // The rows are read back by other lanes of this wave.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + rl;
+      const u32x4 v = *(const u32x4*)(stage + r * kStageCols + ((c ^ swz<kStageCols>(r)) << 3));
+      if (r < nrows) *(u32x4*)(out + (int64_t)r * st + q * kStageCols + 8 * c) = v;
+    }
+  }
+  // A caller may keep other data in the area (an index claimed later):
+  // no later access may be moved above these.
+  asm volatile("" ::: "memory");
+}
+
 // All loads of a tile at once.
 template <int D, int ROWS, int NT = 256>
 __device__ __forceinline__ void issue_tile(const uint16_t* head_row0, int nrows, int64_t st,
