@@ -9,7 +9,7 @@
 //                tensor's strides, which is why the workspace is sized from
 //                LSE's full span.
 //   dkdv         one item = (kv group, 128-key tile, kv head).  Each wave keeps
-//                32 keys of K and V in registers; 32-row query tiles of every
+//                32 keys of K and V in registers; 64-row query tiles of every
 //                query head of the GQA group and every member sequence of the
 //                kv group (sequences binding the same K/V rows) stream through
 //                LDS, double-buffered:
@@ -21,7 +21,8 @@
 //                causal band streaming through LDS like the forward:
 //                  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T o (dP^T - delta),
 //                  dQ^T += K^T dS^T  (K read transposed);
-//                dQ = scale * dQ stored as bf16 for valid rows.
+//                dQ = scale * dQ stored as bf16 for valid rows, whole row
+//                segments at a time through a per-wave LDS area.
 // dQ is accumulated in registers by a query-major pass instead of fp32
 // atomics from the key-major pass: that recomputes S and dP once more (14*D
 // flops per pair instead of 10*D) but writes every dQ element once.

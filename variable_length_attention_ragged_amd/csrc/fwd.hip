@@ -21,7 +21,8 @@
 //                    only when a row's tile max passes it by more than 8;
 //   O^T += V^T P^T   MFMA, V read transposed from LDS (ds_read_b64_tr_b16),
 //                    P taken straight from the S^T accumulators.
-// Query rows past Lq load zeros and are never stored.
+// Query rows past Lq load zeros and are never stored; O leaves through a
+// per-wave LDS area as whole row segments.
 #include <type_traits>
 
 #include "common.h"
