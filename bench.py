@@ -15,6 +15,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -83,17 +84,31 @@ def fwd_bytes(batch) -> int:
             + q_rows * batch.h_q * 4)
 
 
+_C_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def _code_tokens(text: str) -> str:
+    """C/HIP source with comments removed and whitespace runs collapsed, so
+    that a comment-only edit leaves the fingerprint (and the machine code)
+    unchanged.  String literals in these sources hold no comment markers."""
+    return " ".join(_C_COMMENT.sub(" ", text).split())
+
+
 def kernel_fingerprint() -> str:
-    """sha256 over the HIP sources and the build script (which holds the
-    compiler flags), as recorded next to the profiled traffic."""
+    """sha256 over the code of the HIP sources (comments and layout ignored)
+    and the build script (which holds the compiler flags), as recorded next
+    to the profiled traffic."""
     import glob
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "variable_length_attention_ragged_amd")
-    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
+    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))):
         h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(b"build.py")
+        h.update(f.read())
     return h.hexdigest()
 
 
