@@ -28,18 +28,33 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
-# --workload: (workloads function, description)
+# --workload: (workloads function, description, passes).  The first is the
+# headline configuration; the others time the same kernels on the other
+# synthetic configurations, each with the passes its configuration defines.
 WORKLOADS = {
     "packed_causal": ("config2", "packed causal THD: 16 sequences, lengths U[128,4096] "
                                  "(seed 1002), H_q=H_kv=32, D=128, top-left causal, "
-                                 "head-major LSE; fwd+bwd"),
+                                 "head-major LSE; fwd+bwd", "fwd+bwd"),
     "sliding_window": ("config2_window", "packed causal THD with a sliding window: the "
                                          "packed causal lengths (seed 1002), H_q=H_kv=32, "
                                          "D=128, top-left causal, window (1024, 0), "
-                                         "head-major LSE; fwd+bwd"),
+                                         "head-major LSE; fwd+bwd", "fwd+bwd"),
     "packed_causal_f16": ("config2_f16", "packed causal THD in fp16: the packed causal "
                                          "lengths (seed 1002), H_q=H_kv=32, D=128, top-left "
-                                         "causal, head-major LSE; fwd+bwd"),
+                                         "causal, head-major LSE; fwd+bwd", "fwd+bwd"),
+    "padded_gqa": ("config3", "padded THD with GQA: 32 sequences, lengths U[64,2048], "
+                              "U{0..63} NaN pad rows after each sequence, drawn separately "
+                              "for Q/O and K/V (seed 1003), H_q=32, H_kv=8, D=128, "
+                              "padding_causal, token-major LSE; fwd+bwd", "fwd+bwd"),
+    "mixed_policy": ("config4", "mixed per-sequence mask policy: 64 sequences, Lq U[32,1024], "
+                                "Lk = Lq + U[0,1024], policy U{padding, causal top-left, "
+                                "causal bottom-right} as a device int8 tensor (seed 1004), "
+                                "H=16, D=128, token-major LSE; fwd", "fwd"),
+    "long_context_cp": ("config5", "long-context causal query chunks: 2 documents of 65536 "
+                                   "keys, each queried by two 4096-row chunks at absolute "
+                                   "key offsets 4096 and 61440 (per-segment q causal "
+                                   "offsets; the two chunks of a document bind the same K/V "
+                                   "rows), H=16, D=128, head-major LSE; fwd+bwd", "fwd+bwd"),
 }
 
 
@@ -196,22 +211,25 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
         return 0
-    batch = getattr(workloads, WORKLOADS[args.workload][0])(with_grad=True)
-    dev = DeviceBatch(batch, with_grad=True)
+    fn, desc, passes = WORKLOADS[args.workload]
+    with_bwd = passes == "fwd+bwd"
+    batch = getattr(workloads, fn)(with_grad=with_bwd)
+    dev = DeviceBatch(batch, with_grad=with_bwd)
     fwd_ws = torch.empty(dev.fwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
-    bwd_ws = torch.empty(dev.bwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
 
     pairs = int(pairs_per_head(batch).sum())
     fwd_flops = 4.0 * batch.dim * batch.h_q * pairs
-    bwd_flops = 10.0 * batch.dim * batch.h_q * pairs
+    bwd_flops = 10.0 * batch.dim * batch.h_q * pairs if with_bwd else 0.0
 
     # One step, one event between consecutive kernels (all on the current
     # stream, which the library launches on).
     stages = [("setup (fwd)", lambda: dev.fwd_setup(workspace=fwd_ws)),
-              ("fwd_kernel", lambda: dev.fwd_stage("varlen_attn_fwd_attention", workspace=fwd_ws)),
-              ("setup (bwd)", lambda: dev.bwd_setup(workspace=bwd_ws)),
-              ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq", workspace=bwd_ws)),
-              ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws))]
+              ("fwd_kernel", lambda: dev.fwd_stage("varlen_attn_fwd_attention", workspace=fwd_ws))]
+    if with_bwd:
+        bwd_ws = torch.empty(dev.bwd_layout().total_bytes, dtype=torch.uint8, device="cuda")
+        stages += [("setup (bwd)", lambda: dev.bwd_setup(workspace=bwd_ws)),
+                   ("bwd_dq_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dq", workspace=bwd_ws)),
+                   ("bwd_dkdv_kernel", lambda: dev.bwd_stage("varlen_attn_bwd_dkdv", workspace=bwd_ws))]
 
     def step(ev=None):
         for n, (_, run) in enumerate(stages):
@@ -240,7 +258,6 @@ def main(argv=None) -> int:
     stage_ms = {name: float(np.mean([e[n].elapsed_time(e[n + 1]) for e in evs]))
                 for n, (name, _) in enumerate(stages)}
     fwd_kernel_ms = stage_ms["fwd_kernel"]
-    dkdv_ms = stage_ms["bwd_dkdv_kernel"]
     bwd_ms = sum(v for k, v in stage_ms.items() if k.startswith("bwd") or k == "setup (bwd)")
     fwd_ms = stage_ms["fwd_kernel"] + stage_ms["setup (fwd)"]
     dominant = max(stage_ms, key=stage_ms.get)
@@ -253,6 +270,32 @@ def main(argv=None) -> int:
     fwd_tflops = fwd_flops / (fwd_kernel_ms * 1e-3) / 1e12
     dom_tflops = kernel_flops.get(dominant, 0.0) / (stage_ms[dominant] * 1e-3) / 1e12
     value = (fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12
+    fwd_gb = fwd_bytes(batch) / 1e9
+    config = {
+        "workload": desc,
+        "passes": passes,
+        "tokens": int(batch.lq.sum()),
+        "pairs_per_head": pairs,
+        "fwd_gflop": round(fwd_flops / 1e9, 2),
+        "bwd_gflop": round(bwd_flops / 1e9, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        # compulsory bytes of the forward (Q, K, V read once, O and LSE
+        # written) over the forward kernel's time: the HBM side of its roofline
+        "fwd_compulsory_gb": round(fwd_gb, 4),
+        "fwd_compulsory_gbs": round(fwd_gb / (fwd_kernel_ms * 1e-3), 1),
+    }
+    if with_bwd:
+        config.update({
+            "bwd_ms": round(bwd_ms, 4),
+            "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+            "bwd_dkdv_tflops": round(0.8 * bwd_flops / (stage_ms["bwd_dkdv_kernel"] * 1e-3) / 1e12, 2),
+            "bwd_dq_tflops": round(0.2 * bwd_flops / (stage_ms["bwd_dq_kernel"] * 1e-3) / 1e12, 2),
+        })
+    config["step_pct_peak"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
+    config["wall_s_timed"] = round(t_wall, 3)
     line = {
         "metric": "varlen attention fwd/bwd TFLOP/s (causal-aware) and % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -266,23 +309,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": batch.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": WORKLOADS[args.workload][1],
-            "tokens": int(batch.lq.sum()),
-            "pairs_per_head": pairs,
-            "fwd_gflop": round(fwd_flops / 1e9, 2),
-            "bwd_gflop": round(bwd_flops / 1e9, 2),
-            "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-            "fwd_ms": round(fwd_ms, 4),
-            "bwd_ms": round(bwd_ms, 4),
-            "fwd_tflops": round(fwd_tflops, 2),
-            "fwd_pct_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
-            "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
-            "bwd_dkdv_tflops": round(0.8 * bwd_flops / (dkdv_ms * 1e-3) / 1e12, 2),
-            "bwd_dq_tflops": round(0.2 * bwd_flops / (stage_ms["bwd_dq_kernel"] * 1e-3) / 1e12, 2),
-            "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-            "wall_s_timed": round(t_wall, 3),
-        },
+        "config": config,
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
