@@ -33,3 +33,23 @@ def test_bench_workloads_are_the_named_configurations():
     assert win.window.tolist() == [[-1, -1], [1024, 0], [-1, -1]]
     # the window removes pairs of rows more than 1024 keys past their sequence start
     assert bench.pairs_per_head(win).sum() < bench.pairs_per_head(full).sum()
+
+
+def test_long_context_pairs_match_the_closed_form():
+    # Each document's two 4096-row chunks start at absolute keys 4096 and
+    # 61440; row i of a chunk at offset o sees keys 0 .. o + i, so the chunk
+    # contributes sum_{i<4096} (o + 1 + i) pairs per head.
+    batch = workloads.config5(with_grad=False)
+    per_chunk = {o: 4096 * (o + 1) + 4095 * 4096 // 2 for o in (4096, 61440)}
+    assert per_chunk == {4096: 25_167_872, 61440: 260_048_896}
+    assert bench.pairs_per_head(batch).tolist() == [per_chunk[4096], per_chunk[61440]] * 2
+    assert int(bench.pairs_per_head(batch).sum()) == 570_433_536
+
+
+def test_every_bench_workload_resolves_with_its_passes():
+    for name, (fn, desc, passes) in bench.WORKLOADS.items():
+        assert callable(getattr(workloads, fn)), name
+        assert passes in ("fwd", "fwd+bwd") and desc, name
+    # the mixed-policy configuration is defined as a forward-only launch
+    assert bench.WORKLOADS["mixed_policy"][2] == "fwd"
+    assert bench.WORKLOADS["packed_causal"][2] == "fwd+bwd"
