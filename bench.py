@@ -32,25 +32,25 @@ PEAK_HBM_GBS = 8000.0
 # headline configuration; the others time the same kernels on the other
 # synthetic configurations, each with the passes its configuration defines.
 WORKLOADS = {
-    "packed_causal": ("config2", "packed causal THD: 16 sequences, lengths U[128,4096] "
+    "packed_causal": ("packed_causal", "packed causal THD: 16 sequences, lengths U[128,4096] "
                                  "(seed 1002), H_q=H_kv=32, D=128, top-left causal, "
                                  "head-major LSE; fwd+bwd", "fwd+bwd"),
-    "sliding_window": ("config2_window", "packed causal THD with a sliding window: the "
+    "sliding_window": ("packed_causal_window", "packed causal THD with a sliding window: the "
                                          "packed causal lengths (seed 1002), H_q=H_kv=32, "
                                          "D=128, top-left causal, window (1024, 0), "
                                          "head-major LSE; fwd+bwd", "fwd+bwd"),
-    "packed_causal_f16": ("config2_f16", "packed causal THD in fp16: the packed causal "
+    "packed_causal_f16": ("packed_causal_f16", "packed causal THD in fp16: the packed causal "
                                          "lengths (seed 1002), H_q=H_kv=32, D=128, top-left "
                                          "causal, head-major LSE; fwd+bwd", "fwd+bwd"),
-    "padded_gqa": ("config3", "padded THD with GQA: 32 sequences, lengths U[64,2048], "
+    "padded_gqa": ("padded_gqa", "padded THD with GQA: 32 sequences, lengths U[64,2048], "
                               "U{0..63} NaN pad rows after each sequence, drawn separately "
                               "for Q/O and K/V (seed 1003), H_q=32, H_kv=8, D=128, "
                               "padding_causal, token-major LSE; fwd+bwd", "fwd+bwd"),
-    "mixed_policy": ("config4", "mixed per-sequence mask policy: 64 sequences, Lq U[32,1024], "
+    "mixed_policy": ("mixed_policy", "mixed per-sequence mask policy: 64 sequences, Lq U[32,1024], "
                                 "Lk = Lq + U[0,1024], policy U{padding, causal top-left, "
                                 "causal bottom-right} as a device int8 tensor (seed 1004), "
                                 "H=16, D=128, token-major LSE; fwd", "fwd"),
-    "long_context_cp": ("config5", "long-context causal query chunks: 2 documents of 65536 "
+    "long_context_cp": ("long_context_cp", "long-context causal query chunks: 2 documents of 65536 "
                                    "keys, each queried by two 4096-row chunks at absolute "
                                    "key offsets 4096 and 61440 (per-segment q causal "
                                    "offsets; the two chunks of a document bind the same K/V "

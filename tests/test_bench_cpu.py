@@ -27,8 +27,8 @@ def test_pairs_per_head_counts_the_oracle_mask(seed, qco, window):
 
 
 def test_bench_workloads_are_the_named_configurations():
-    full = workloads.config2()
-    win = workloads.config2_window()
+    full = workloads.packed_causal()
+    win = workloads.packed_causal_window()
     assert np.array_equal(full.lq, win.lq) and full.window is None
     assert win.window.tolist() == [[-1, -1], [1024, 0], [-1, -1]]
     # the window removes pairs of rows more than 1024 keys past their sequence start
@@ -39,7 +39,7 @@ def test_long_context_pairs_match_the_closed_form():
     # Each document's two 4096-row chunks start at absolute keys 4096 and
     # 61440; row i of a chunk at offset o sees keys 0 .. o + i, so the chunk
     # contributes sum_{i<4096} (o + 1 + i) pairs per head.
-    batch = workloads.config5(with_grad=False)
+    batch = workloads.long_context_cp(with_grad=False)
     per_chunk = {o: 4096 * (o + 1) + 4095 * 4096 // 2 for o in (4096, 61440)}
     assert per_chunk == {4096: 25_167_872, 61440: 260_048_896}
     assert bench.pairs_per_head(batch).tolist() == [per_chunk[4096], per_chunk[61440]] * 2

@@ -77,10 +77,10 @@ def _check_setup(batch, backward):
 
 
 SETUP_CASES = [
-    ("cfg1", lambda: workloads.config1(causal=True)),
-    ("cfg3", lambda: workloads.config3()),
-    ("cfg4", lambda: workloads.config4(with_grad=True)),
-    ("cfg5_small", lambda: workloads.config5(doc_len=4096, chunk=512, offsets=(512, 3584))),
+    ("tiny_padded", lambda: workloads.tiny_padded_thd(causal=True)),
+    ("padded_gqa", lambda: workloads.padded_gqa()),
+    ("mixed_policy", lambda: workloads.mixed_policy(with_grad=True)),
+    ("long_context_small", lambda: workloads.long_context_cp(doc_len=4096, chunk=512, offsets=(512, 3584))),
 ] + [(f"random{s}", (lambda s=s: workloads.random_batch(s, batch=9, max_len=300,
                                                          q_causal_offset=bool(s % 2))))
      for s in range(100, 106)] + [
@@ -93,7 +93,7 @@ SETUP_CASES = [
                                                          q_causal_offset=bool(s % 2),
                                                          window="random")))
      for s in range(120, 126)] + [
-    ("cfg5_small_window", lambda: _windowed(workloads.config5(doc_len=4096, chunk=512,
+    ("long_context_small_window", lambda: _windowed(workloads.long_context_cp(doc_len=4096, chunk=512,
                                                               offsets=(512, 3584)),
                                             [[-1, -1], [700, 0], [-1, -1]])),
 ]
@@ -116,8 +116,8 @@ def test_setup_bit_exact(name, make, backward):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("lse_kind", ["token", "head"])
 def test_config1_fwd_bwd(causal, lse_kind):
-    say(f"[cfg1] causal={causal} lse={lse_kind}")
-    batch = workloads.config1(causal=causal, lse_kind=lse_kind)
+    say(f"[tiny padded] causal={causal} lse={lse_kind}")
+    batch = workloads.tiny_padded_thd(causal=causal, lse_kind=lse_kind)
     dev = _dev(batch)
     dev.fwd()
     dev.bwd()
@@ -187,9 +187,9 @@ def test_sliding_window_long_sequences(window):
 def test_window_with_aliased_kv_segments():
     """Context-parallel chunks of one document with a causal window: the
     caller's offsets anchor each chunk's band, and the chunks' dK/dV sum."""
-    batch = _windowed(workloads.config5(doc_len=1024, chunk=256, offsets=(256, 768)),
+    batch = _windowed(workloads.long_context_cp(doc_len=1024, chunk=256, offsets=(256, 768)),
                       [[-1, -1], [300, 0], [-1, -1]])
-    say("[window alias] cfg5 shape, doc 1024 chunk 256, window 300")
+    say("[window alias] long-context shape, doc 1024 chunk 256, window 300")
     dev = _dev(batch)
     dev.fwd()
     dev.bwd()
@@ -219,7 +219,7 @@ def test_fp16_random_fwd_bwd(seed, dim, window):
 def test_fp16_full_size_sampled():
     """The packed causal workload's shape in fp16: sampled forward rows and the
     gradients of one kv head."""
-    b16 = workloads.config2(with_grad=True)
+    b16 = workloads.packed_causal(with_grad=True)
     batch = workloads.build("packed_causal_f16", 1102, 32, 32, 128, b16.lq, b16.lk,
                             b16.layouts["q"].start_rows, b16.layouts["k"].start_rows,
                             default_policy=workloads.CAUSAL_TOP_LEFT, lse_kind="head",
@@ -267,8 +267,8 @@ def test_gqa_groups_of_four_fwd_bwd():
 
 
 def test_aliased_kv_segments_sum_gradients():
-    batch = workloads.config5(doc_len=1024, chunk=256, offsets=(256, 768))
-    say("[alias] cfg5 shape, doc 1024 chunk 256")
+    batch = workloads.long_context_cp(doc_len=1024, chunk=256, offsets=(256, 768))
+    say("[alias] long-context shape, doc 1024 chunk 256")
     dev = _dev(batch)
     dev.fwd()
     dev.bwd()
@@ -524,15 +524,15 @@ def _check_pads_untouched(batch, dev, names):
         assert np.array_equal(got[~valid].view(np.uint8), pre[~valid].view(np.uint8)), n
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_forward_sampled(cfg):
-    batch = workloads.CONFIGS[cfg](with_grad=False)
-    say(f"[full fwd] config {cfg}: B={batch.batch} lq_sum={int(batch.lq.sum())}")
+@pytest.mark.parametrize("name", ["packed_causal", "padded_gqa", "mixed_policy", "long_context_cp"])
+def test_full_size_forward_sampled(name):
+    batch = workloads.BY_NAME[name](with_grad=False)
+    say(f"[full fwd] {name}: B={batch.batch} lq_sum={int(batch.lq.sum())}")
     dev = _dev(batch, with_grad=False)
     dev.fwd()
     torch.cuda.synchronize()
     assert int(dev.status.item()) == 0
-    _check_sampled_fwd(batch, dev, seed=cfg)
+    _check_sampled_fwd(batch, dev, seed=batch.seed)
     _check_pads_untouched(batch, dev, ("o", "lse"))
 
 
@@ -540,7 +540,7 @@ def test_full_size_sliding_window_sampled():
     """The benchmark's sliding-window workload at full size, in the launch
     configuration the benchmark times: sampled forward rows and the complete
     gradients of one kv head."""
-    batch = workloads.config2_window(with_grad=True)
+    batch = workloads.packed_causal_window(with_grad=True)
     say(f"[full window] B={batch.batch} lq_sum={int(batch.lq.sum())} window={batch.window.tolist()}")
     dev = _dev(batch, with_grad=True)
     dev.fwd()
@@ -558,10 +558,14 @@ def test_full_size_sliding_window_sampled():
     _check_pads_untouched(batch, dev, ("o", "lse", "dq", "dk", "dv"))
 
 
-@pytest.mark.parametrize("cfg,kv_heads", [(3, [0, 5]), (5, [3])])
-def test_full_size_backward_head_subset(cfg, kv_heads):
-    batch = workloads.CONFIGS[cfg](with_grad=True)
-    say(f"[full bwd] config {cfg} kv heads {kv_heads}")
+@pytest.mark.parametrize("name,kv_heads", [("packed_causal", [0, 17]), ("padded_gqa", [0, 5]),
+                                           ("long_context_cp", [3])])
+def test_full_size_backward_head_subset(name, kv_heads):
+    """Complete gradients of a few kv heads at full size, in the launch
+    configuration the benchmark times (the packed causal workload is its
+    headline)."""
+    batch = workloads.BY_NAME[name](with_grad=True)
+    say(f"[full bwd] {name} kv heads {kv_heads}")
     dev = _dev(batch, with_grad=True)
     dev.fwd()
     dev.bwd()

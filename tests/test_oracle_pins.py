@@ -36,7 +36,7 @@ def _run_fwd(batch, outputs=None, **kw):
 
 def test_padded_thd_worked_example_addresses_bound_offsets():
     g = _golden("padded_thd_13row.json")
-    batch = workloads.config1(causal=False)
+    batch = workloads.tiny_padded_thd(causal=False)
     assert list(batch.cu_q) == g["cu_seqlens"]
     start = batch.layouts["q"].start_rows
     assert list(start) == g["cu_seqlens_padded"]
@@ -57,7 +57,7 @@ def test_padded_thd_worked_example_addresses_bound_offsets():
 
 def test_padded_thd_worked_example_identifier_rows_do_not_matter():
     g = _golden("padded_thd_13row.json")
-    batch = workloads.config1(causal=True)
+    batch = workloads.tiny_padded_thd(causal=True)
     base = _run_fwd(batch)
     # put large finite values into the identifier rows of Q/K/V: nothing changes
     for n in ("q", "k", "v"):
@@ -79,7 +79,7 @@ def test_prefix_of_lengths_addressing_is_the_defect():
     """The mis-derivation re-addresses sequence 1 at the identifier row 3; the
     NaN there poisons its output.  The oracle must not do that."""
     g = _golden("padded_thd_13row.json")
-    batch = workloads.config1(causal=False)
+    batch = workloads.tiny_padded_thd(causal=False)
     prob, t = oracle.from_batch(batch)
     wrong_rows = np.asarray(g["cu_seqlens"], np.int64)
     for n in ("q", "k", "v", "o"):

@@ -217,7 +217,7 @@ def build(name, seed, h_q, h_kv, dim, lq, lk, q_start, kv_start, *, default_poli
 
 # ---------------------------------------------------------------- workloads
 
-def config1(causal: bool = False, lse_kind: str = "token", seed: int = 1001) -> Batch:
+def tiny_padded_thd(causal: bool = False, lse_kind: str = "token", seed: int = 1001) -> Batch:
     """Three sequences [3, 2, 4] with one identifier row after each:
     rows [a a a 1 b b 2 2 c c c c 3], cu_seqlens [0,3,5,9],
     cu_seqlens_padded [0,4,8,13]."""
@@ -227,7 +227,7 @@ def config1(causal: bool = False, lse_kind: str = "token", seed: int = 1001) -> 
                  default_policy=CAUSAL_TOP_LEFT if causal else PADDING, lse_kind=lse_kind)
 
 
-def config2(seed: int = 1002, with_grad: bool = False) -> Batch:
+def packed_causal(seed: int = 1002, with_grad: bool = False) -> Batch:
     rng = np.random.default_rng(seed)
     lens = rng.integers(128, 4096, size=16, endpoint=True)
     start = _prefix(lens)
@@ -235,16 +235,16 @@ def config2(seed: int = 1002, with_grad: bool = False) -> Batch:
                  default_policy=CAUSAL_TOP_LEFT, lse_kind="head", with_grad=with_grad)
 
 
-def config2_window(seed: int = 1002, with_grad: bool = False, left: int = 1024) -> Batch:
+def packed_causal_window(seed: int = 1002, with_grad: bool = False, left: int = 1024) -> Batch:
     """The packed causal workload with a bounded causal window: each row sees
-    itself and the ``left`` keys before it (the lengths and data of config 2)."""
-    b = config2(seed, with_grad)
+    itself and the ``left`` keys before it (the lengths and data of the packed causal workload)."""
+    b = packed_causal(seed, with_grad)
     b.name = f"packed_causal_window{left}_h32_d128"
     b.window = np.array([[-1, -1], [left, 0], [-1, -1]], np.int32)
     return b
 
 
-def config2_f16(seed: int = 1002, with_grad: bool = False) -> Batch:
+def packed_causal_f16(seed: int = 1002, with_grad: bool = False) -> Batch:
     """The packed causal workload (same lengths and layout) in IEEE fp16."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(128, 4096, size=16, endpoint=True)
@@ -254,7 +254,7 @@ def config2_f16(seed: int = 1002, with_grad: bool = False) -> Batch:
                  dtype="f16")
 
 
-def config3(seed: int = 1003, with_grad: bool = True) -> Batch:
+def padded_gqa(seed: int = 1003, with_grad: bool = True) -> Batch:
     rng = np.random.default_rng(seed)
     lens = rng.integers(64, 2048, size=32, endpoint=True)
     gq = rng.integers(0, 63, size=32, endpoint=True)
@@ -264,7 +264,7 @@ def config3(seed: int = 1003, with_grad: bool = True) -> Batch:
                  default_policy=CAUSAL_TOP_LEFT, lse_kind="token", with_grad=with_grad)
 
 
-def config4(seed: int = 1004, with_grad: bool = False) -> Batch:
+def mixed_policy(seed: int = 1004, with_grad: bool = False) -> Batch:
     rng = np.random.default_rng(seed)
     lq = rng.integers(32, 1024, size=64, endpoint=True)
     lk = lq + rng.integers(0, 1024, size=64, endpoint=True)
@@ -273,7 +273,7 @@ def config4(seed: int = 1004, with_grad: bool = False) -> Batch:
                  default_policy=PADDING, policy=policy, lse_kind="token", with_grad=with_grad)
 
 
-def config5(seed: int = 1005, with_grad: bool = True, doc_len: int = 65536,
+def long_context_cp(seed: int = 1005, with_grad: bool = True, doc_len: int = 65536,
             chunk: int = 4096, offsets=(4096, 61440)) -> Batch:
     """Two documents of ``doc_len`` keys; each queried by two ``chunk``-row
     segments whose first query sits at absolute key ``offsets[i]``.  Both
@@ -289,7 +289,9 @@ def config5(seed: int = 1005, with_grad: bool = True, doc_len: int = 65536,
                  with_grad=with_grad)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# The five measured workloads by name.
+BY_NAME = {"tiny_padded_thd": tiny_padded_thd, "packed_causal": packed_causal,
+           "padded_gqa": padded_gqa, "mixed_policy": mixed_policy, "long_context_cp": long_context_cp}
 
 
 def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4, h_kv: int = 2,
