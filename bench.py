@@ -187,7 +187,7 @@ def main(argv=None) -> int:
                          "(calibrates HBM byte counters against a known size) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got "
               f"--gpus {args.gpus}", file=sys.stderr)
         return 2
 
