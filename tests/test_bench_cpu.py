@@ -53,3 +53,13 @@ def test_every_bench_workload_resolves_with_its_passes():
     # the mixed-policy configuration is defined as a forward-only launch
     assert bench.WORKLOADS["mixed_policy"][2] == "fwd"
     assert bench.WORKLOADS["packed_causal"][2] == "fwd+bwd"
+
+
+def test_kernel_fingerprint_ignores_comments_but_not_code():
+    a = "int f(int x) {  // doubles x\n  return 2 * x; /* no overflow\n check */\n}\n"
+    b = "int f(int x) {\n    return 2 * x;\n}"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench._code_tokens(a) == bench._code_tokens(b)
+    assert bench._code_tokens(a) != bench._code_tokens(c)
+    # the recorded traffic is looked up under the current sources' fingerprint
+    assert len(bench.kernel_fingerprint()) == 64
