@@ -12,14 +12,14 @@ Modules:
   sizing     the span of a strided view, by definition
 """
 from .attention import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, PADDING, ST_BAD_OFFSET,
-                        ST_BAD_POLICY, ST_LIST_OVERFLOW, ST_NEG_LENGTH, ST_OUT_OF_SPAN,
-                        Problem, Tensor, backward, bf16_bits_to_f64, bits_to_f64, forward,
-                        forward_rows, sequence_info)
+                        ST_BAD_POLICY, ST_KV_OVERLAP, ST_LIST_OVERFLOW, ST_NEG_LENGTH,
+                        ST_OUT_OF_SPAN, Problem, Tensor, backward, bf16_bits_to_f64,
+                        bits_to_f64, forward, forward_rows, kv_overlap, sequence_info)
 from . import sizing, worklist
 
 __all__ = [
     "CAUSAL_BOTTOM_RIGHT", "CAUSAL_TOP_LEFT", "PADDING", "ST_BAD_OFFSET", "ST_BAD_POLICY",
-    "ST_LIST_OVERFLOW", "ST_NEG_LENGTH", "ST_OUT_OF_SPAN", "Problem", "Tensor", "backward",
+    "ST_KV_OVERLAP", "kv_overlap", "ST_LIST_OVERFLOW", "ST_NEG_LENGTH", "ST_OUT_OF_SPAN", "Problem", "Tensor", "backward",
     "bf16_bits_to_f64", "bits_to_f64", "forward", "forward_rows", "sequence_info", "sizing", "worklist",
     "from_batch",
 ]

@@ -72,6 +72,7 @@ ST_BAD_OFFSET = 1 << 1     # ragged offset negative or not 16-byte aligned
 ST_OUT_OF_SPAN = 1 << 2    # a row of the sequence would leave the buffer
 ST_BAD_POLICY = 1 << 3     # policy value outside {0, 1, 2}
 ST_LIST_OVERFLOW = 1 << 4  # more tiles than the output buffer can hold
+ST_KV_OVERLAP = 1 << 5     # backward: key-side gradient rows shared with another kv group
 
 ROW_BLOCK = 512
 
@@ -331,6 +332,43 @@ def forward_rows(prob: Problem, q: Tensor, k: Tensor, v: Tensor, b: int, h: int,
     return out_o, out_l
 
 
+def kv_overlap(infos: list, k: Tensor, v: Tensor, dk: Tensor, dv: Tensor) -> list:
+    """Which sequences the backward must skip because their key-side gradient
+    rows collide with those of other sequences.
+
+    Several query segments may bind the same key rows: context-parallel query
+    chunks of one document share its key prefix (Megatron-LM PR #14, commit
+    message), and their dK/dV are the sums over those segments.  Segments
+    whose K, V, dK and dV offsets are all identical form one kv group,
+    wherever they sit in the batch.  A group owns rows [0, Lk_max) of its dK
+    and dV tensors, Lk_max being its members' largest key length, i.e. the
+    element range [offset, offset + Lk_max * stride_t) of each.  When two
+    groups' ranges intersect in dK or in dV, their gradients cannot both be
+    stored (one would overwrite the other without any error: the silent
+    mis-service of the cudnn-frontend issue on padded THD, "Concrete
+    failure"), so every member of both groups is flagged instead.  Only
+    valid sequences with key rows take part.  Returns a list of bools."""
+    B = len(infos)
+    members = [b for b in range(B) if infos[b].valid and infos[b].lk > 0]
+    key = {b: tuple(int(t.ragged[b]) for t in (k, v, dk, dv)) for b in members}
+    lk_max = {}
+    for b in members:
+        lk_max[key[b]] = max(lk_max.get(key[b], 0), infos[b].lk)
+    groups = sorted(lk_max)
+    hit = set()
+    for ga in groups:
+        for gb in groups:
+            if ga == gb:
+                continue
+            for pos, t in ((2, dk), (3, dv)):
+                a0, b0 = ga[pos], gb[pos]
+                a1 = a0 + lk_max[ga] * t.stride_t
+                b1 = b0 + lk_max[gb] * t.stride_t
+                if a0 < b1 and b0 < a1:
+                    hit.add(ga)
+    return [b in key and key[b] in hit for b in range(B)]
+
+
 def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Tensor,
              do: Tensor, dq: Tensor, dk: Tensor, dv: Tensor, kv_heads=None):
     """Oracle backward: the exact gradients of sum(dO * O) with respect to
@@ -342,7 +380,8 @@ def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Ten
     query reaches them (their gradient is 0).  ``kv_heads`` restricts the work
     to whole GQA groups.  ``o`` and ``lse`` (the forward's outputs, inputs of
     the backward) take part in the validation of each sequence only; the
-    oracle recomputes both in fp64."""
+    oracle recomputes both in fp64.  Sequences that ``kv_overlap`` flags get
+    ST_KV_OVERLAP and are skipped like any invalid sequence."""
     dq_out, dk_out, dv_out = dq.values(), dk.values(), dv.values()
     dq_w = np.zeros(dq.span, bool)
     dk_w = np.zeros(dk.span, bool)
@@ -350,14 +389,17 @@ def backward(prob: Problem, q: Tensor, k: Tensor, v: Tensor, o: Tensor, lse: Ten
     group = prob.h_q // prob.h_kv
     gsel = range(prob.h_kv) if kv_heads is None else kv_heads
     status = 0
-    infos = []
     # Key-side gradients accumulate in fp64 over every segment and q head that
     # reaches them, so that segments binding the same K/V rows sum.
     dk_acc = np.zeros(dk.span)
     dv_acc = np.zeros(dv.span)
+    infos = [sequence_info(prob, [q, o, lse, do, dq], [k, v, dk, dv], b)
+             for b in range(prob.batch)]
+    for b, clash in enumerate(kv_overlap(infos, k, v, dk, dv)):
+        if clash:
+            infos[b].status |= ST_KV_OVERLAP
     for b in range(prob.batch):
-        info = sequence_info(prob, [q, o, lse, do, dq], [k, v, dk, dv], b)
-        infos.append(info)
+        info = infos[b]
         status |= info.status
         if not info.valid:
             continue

@@ -27,22 +27,32 @@ are this library's own design:
   key range of the tile being ``kv_begin = clamp(row_start + lo, 0, lk)`` (its
   first row's lower bound) to ``kv_end = clamp(row_end + hi, 0, lk)`` (its last
   row's upper bound plus one).
-* Backward kv-tile list (int32 quadruple (b_first, n_members, u, lk_max) per
-  tile of ``bn_b`` key rows of a kv group): a kv group is a maximal run of
-  consecutive valid sequences with ``lk > 0`` whose K, V, dK and dV bases are
-  all equal (segments binding the same K/V rows, e.g. context-parallel query
-  chunks of one document).  Groups are ordered by descending cost (sum of the
-  members' costs under the backward tile sizes) then ascending b_first; tiles
-  of a group in ascending u over ``ceil(lk_max / bn_b)``.
+* Backward kv groups: the valid sequences with ``lk > 0`` whose K, V, dK and
+  dV bases are all equal, wherever they sit in the batch (segments binding the
+  same K/V rows, e.g. context-parallel query chunks of one document).  Groups
+  whose dK or dV row ranges intersect (``attention.kv_overlap``) are dropped:
+  their members get ST_KV_OVERLAP, lose the valid flag, store hi = lo = 0 and
+  leave both lists (the forward list of a backward setup feeds the dQ pass).
+  The remaining groups are ordered by descending cost (sum of the members'
+  costs under the backward tile sizes) then ascending first member.
+* Member list (int32 per member): each group's members in ascending index,
+  groups in that order.
+* Backward kv-tile list (int32 quadruple (m_start, n_members, u, lk_max) per
+  tile of ``bn_b`` key rows of a group): ``m_start`` is the position of the
+  group's first member in the member list; tiles of a group in ascending u
+  over ``ceil(lk_max / bn_b)``.
 * If a list would exceed its capacity (more tiles than the output buffer's rows
   can hold, which only happens when sequences overlap), the overflow bit is set
   and both tile counts are 0: nothing is computed.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 
-from .attention import ST_LIST_OVERFLOW, Problem, SeqInfo, Tensor, sequence_info
+from .attention import (ST_KV_OVERLAP, ST_LIST_OVERFLOW, Problem, SeqInfo, Tensor, kv_overlap,
+                        sequence_info)
 
 BASE_ORDER = ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")
 
@@ -100,10 +110,13 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
     flags = np.zeros(B, np.int32)
     base = np.zeros((9, B), np.int64)
     status = 0
-    infos = []
+    infos = [sequence_info(prob, q_side, kv_side, b) for b in range(B)]
+    if backward:
+        clash = kv_overlap(infos, *(tensors[n] for n in ("k", "v", "dk", "dv")))
+        infos = [dataclasses.replace(i, status=i.status | ST_KV_OVERLAP) if c else i
+                 for i, c in zip(infos, clash)]
     for b in range(B):
-        info = sequence_info(prob, q_side, kv_side, b)
-        infos.append(info)
+        info = infos[b]
         lq[b], lk[b], pol[b] = info.lq, info.lk, info.policy
         hi[b], lo[b] = band(info)
         flags[b] = (1 if info.valid else 0) | (info.status << 8)
@@ -122,32 +135,26 @@ def setup(prob: Problem, tensors: dict, *, backward: bool, bm: int, bn: int,
         for t in range(ceil_div(infos[b].lq, bm) - 1, -1, -1):
             fwd.append((b, t))
 
-    bwd = []
+    bwd, mlist = [], []
     if backward:
-        groups = []  # (first, n)
-        b = 0
-        while b < B:
-            if not (infos[b].valid and infos[b].lk > 0):
-                b += 1
-                continue
-            first = b
-            while (b + 1 < B and infos[b + 1].valid and infos[b + 1].lk > 0
-                   and all(base[i, b + 1] == base[i, first] for i in (1, 2, 7, 8))):
-                b += 1
-            groups.append((first, b - first + 1))
-            b += 1
-        gcost = [sum(cost_of(m, bm_b, bn_b) for m in range(f, f + n)) for f, n in groups]
-        gorder = sorted(range(len(groups)), key=lambda g: (-gcost[g], groups[g][0]))
-        for g in gorder:
-            f, n = groups[g]
-            lmax = max(infos[m].lk for m in range(f, f + n))
+        groups = {}  # (K, V, dK, dV) bases -> members in ascending index
+        for b in range(B):
+            if infos[b].valid and infos[b].lk > 0:
+                groups.setdefault(tuple(int(base[i, b]) for i in (1, 2, 7, 8)), []).append(b)
+        glist = list(groups.values())
+        gcost = [sum(cost_of(m, bm_b, bn_b) for m in g) for g in glist]
+        for gi in sorted(range(len(glist)), key=lambda x: (-gcost[x], glist[x][0])):
+            g = glist[gi]
+            start = len(mlist)
+            mlist.extend(g)
+            lmax = max(infos[m].lk for m in g)
             for u in range(ceil_div(lmax, bn_b)):
-                bwd.append((f, n, u, lmax))
+                bwd.append((start, len(g), u, lmax))
 
     if len(fwd) > cap_fwd or (backward and len(bwd) > cap_bwd):
         status |= ST_LIST_OVERFLOW
-        fwd, bwd = [], []
+        fwd, bwd, mlist = [], [], []
     return dict(lq=lq, lk=lk, policy=pol, hi=hi, lo=lo, flags=flags, base=base,
                 fwd=np.asarray(fwd, np.int32).reshape(-1, 2),
                 bwd=np.asarray(bwd, np.int32).reshape(-1, 4),
-                status=status, infos=infos)
+                members=np.asarray(mlist, np.int32), status=status, infos=infos)

@@ -455,6 +455,124 @@ def test_aliased_segments_sum_their_kv_gradients():
                                rtol=1e-13, atol=1e-15)
 
 
+def _kv_problem(kv_start, lk, seed=5):
+    """Four query segments of 3 rows (top-left causal with offsets) over key
+    rows placed at ``kv_start`` (start row of each segment's K/V/dK/dV)."""
+    rng = np.random.default_rng(seed)
+    H, D = 1, 4
+    B = len(lk)
+    lq = np.full(B, 3)
+    q_start = np.arange(B + 1) * 3
+    kv_rows = int(max(s + n for s, n in zip(kv_start, lk)))
+    prob = oracle.Problem(H, H, D, 0.5, np.concatenate([[0], np.cumsum(lq)]).astype(np.int32),
+                          np.concatenate([[0], np.cumsum(lk)]).astype(np.int32),
+                          np.ones(B, np.int8), 0, np.full(B, 2, np.int32))
+
+    def mk(rows, start, zero=False):
+        arr = np.zeros(rows * D) if zero else rng.standard_normal(rows * D)
+        return oracle.Tensor(arr, D, D, np.asarray(list(start) + [0], np.int64) * D, H, D)
+
+    q, do = mk(3 * B, q_start[:-1]), mk(3 * B, q_start[:-1])
+    k, v = mk(kv_rows, kv_start), mk(kv_rows, kv_start)
+    o, dq = mk(3 * B, q_start[:-1], True), mk(3 * B, q_start[:-1], True)
+    dk, dv = mk(kv_rows, kv_start, True), mk(kv_rows, kv_start, True)
+    lse = oracle.Tensor(np.zeros(3 * B), 1, 1, np.asarray(q_start, np.int64), H, 1)
+    return prob, q, k, v, o, lse, do, dq, dk, dv
+
+
+def test_partial_kv_overlap_skips_both_groups():
+    """Segments 1 and 2 bind different key rows that intersect (rows 4..9 and
+    8..13): neither group's dK/dV can be stored, so both are skipped with
+    ST_KV_OVERLAP; segments 0 and 3 (disjoint rows) are computed exactly as
+    when 1 and 2 are invalid for another reason."""
+    prob, q, k, v, o, lse, do, dq, dk, dv = _kv_problem([0, 4, 8, 14], [4, 6, 6, 5])
+    g = oracle.backward(prob, q, k, v, o, lse, do, dq, dk, dv)
+    assert g["status"] == oracle.ST_KV_OVERLAP
+    assert [i.valid for i in g["infos"]] == [True, False, False, True]
+    assert not g["dq_written"][3 * 4:9 * 4].any()
+    assert not g["dk_written"][4 * 4:14 * 4].any()
+    prob.policy = np.array([1, 9, 9, 1], np.int8)
+    ref = oracle.backward(prob, q, k, v, o, lse, do, dq, dk, dv)
+    assert ref["status"] == oracle.ST_BAD_POLICY
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(g[n + "_written"], ref[n + "_written"])
+        np.testing.assert_array_equal(g[n], ref[n])
+    # the forward reads K/V only: no overlap rule there
+    f = oracle.forward(prob, q, k, v, o, lse)
+    assert not f["status"] & oracle.ST_KV_OVERLAP
+
+
+def test_touching_kv_ranges_do_not_overlap():
+    prob, q, k, v, o, lse, do, dq, dk, dv = _kv_problem([0, 4, 10, 15], [4, 6, 5, 5])
+    assert oracle.backward(prob, q, k, v, o, lse, do, dq, dk, dv)["status"] == 0
+    assert oracle.kv_overlap(
+        [oracle.sequence_info(prob, [q], [k], b) for b in range(4)], k, v, dk, dv) == [False] * 4
+
+
+def test_interleaved_aliased_segments_sum_like_adjacent_ones():
+    """Segments binding identical key rows form one kv group wherever they sit:
+    the order A0, B0, A1, B1 gives the dK/dV of A0, A1, B0, B1 (up to the
+    order of the fp64 sums)."""
+    a = _kv_problem([0, 8, 0, 8], [8, 8, 8, 8])
+    prob, q, k, v, o, lse, do, dq, dk, dv = a
+    inter = oracle.backward(prob, q, k, v, o, lse, do, dq, dk, dv)
+    assert inter["status"] == 0
+    # move segment 2 (A1) before segment 1 (B0): permute the query-side rows
+    # and the per-segment offsets
+    perm = [0, 2, 1, 3]
+    q2 = oracle.Tensor(q.data, q.stride_t, q.stride_h, q.ragged.copy(), 1, 4)
+    do2 = oracle.Tensor(do.data, do.stride_t, do.stride_h, do.ragged.copy(), 1, 4)
+    kv = [oracle.Tensor(t.data, t.stride_t, t.stride_h, t.ragged.copy(), 1, 4)
+          for t in (k, v, dk, dv)]
+    for t, src in [(q2, q), (do2, do)] + list(zip(kv, (k, v, dk, dv))):
+        t.ragged[:4] = src.ragged[perm]
+    adj = oracle.backward(prob, q2, kv[0], kv[1], o, lse, do2, dq, kv[2], kv[3])
+    assert adj["status"] == 0
+    for n in ("dk", "dv"):
+        np.testing.assert_allclose(inter[n], adj[n], rtol=1e-13, atol=1e-15)
+    # and each document's dK is the sum of its two segments run alone
+    parts = []
+    for keep in (0, 2):
+        p2 = oracle.Problem(1, 1, 4, 0.5, prob.cu_q, prob.cu_kv, prob.policy.copy(), 0,
+                            prob.q_causal_offset)
+        p2.policy[[b for b in range(4) if b != keep]] = 9
+        parts.append(oracle.backward(p2, q, k, v, o, lse, do, dq, dk, dv)["dk"][:8 * 4])
+    np.testing.assert_allclose(inter["dk"][:8 * 4], parts[0] + parts[1], rtol=1e-13,
+                               atol=1e-15)
+
+
+@pytest.mark.parametrize("seed,window,qco,lse_kind", [
+    (71, None, False, "token"), (72, "random", True, "head"), (73, "random", False, "token"),
+    (74, None, True, "head")])
+def test_forward_rows_equals_forward(seed, window, qco, lse_kind):
+    """The row-by-row oracle used for sampled checks at full size gives the
+    same O and LSE as the whole-batch oracle, for every row of every
+    sequence and head: random lengths and gaps, per-sequence policies, GQA,
+    windows, q causal offsets and both LSE layouts (one row's softmax is the
+    same sum whether it sits in a block or alone; only the matrix products'
+    summation order may differ)."""
+    batch = workloads.random_batch(seed, batch=5, max_len=150, h_q=4, h_kv=2, dim=16,
+                                   window=window, q_causal_offset=qco, lse_kind=lse_kind,
+                                   with_grad=False)
+    prob, t = oracle.from_batch(batch)
+    full = oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"])
+    o_view = batch.layouts["o"].view(full["o"])
+    l_view = batch.layouts["lse"].view(full["lse"])[:, :, 0]
+    checked = 0
+    for b in range(batch.batch):
+        lq = int(batch.lq[b])
+        if lq == 0 or not full["infos"][b].valid:
+            continue
+        r0 = int(batch.layouts["o"].start_rows[b])
+        rl = int(batch.layouts["lse"].start_rows[b])
+        for h in range(batch.h_q):
+            o_r, l_r = oracle.forward_rows(prob, t["q"], t["k"], t["v"], b, h, range(lq))
+            np.testing.assert_allclose(o_r, o_view[r0:r0 + lq, h], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(l_r, l_view[rl:rl + lq, h], rtol=1e-12, atol=1e-13)
+            checked += lq
+    assert checked > 200
+
+
 # ----------------------------------------------------------------- validation
 
 def test_invalid_sequences_are_skipped_with_status_bits():

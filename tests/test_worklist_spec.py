@@ -40,11 +40,14 @@ def test_forward_and_backward_lists_by_hand():
     assert s["status"] == 0
     assert s["fwd"].tolist() == [[3, 2], [3, 1], [3, 0], [0, 1], [0, 0], [2, 0]]
     # kv groups: one per valid sequence with lk > 0 (bases all differ), ordered by
-    # the same costs under (bm_b, bn_b) = (4, 2): b3 6, b0 5, b2 4, b1 0.
-    assert s["bwd"].tolist() == [[3, 1, 0, 4], [3, 1, 1, 4],
-                                 [0, 1, 0, 5], [0, 1, 1, 5], [0, 1, 2, 5],
+    # the same costs under (bm_b, bn_b) = (4, 2): b3 6, b0 5, b2 4, b1 0.  The
+    # member list holds them in that order; an entry names its group's first
+    # position in that list.
+    assert s["members"].tolist() == [3, 0, 2, 1]
+    assert s["bwd"].tolist() == [[0, 1, 0, 4], [0, 1, 1, 4],
+                                 [1, 1, 0, 5], [1, 1, 1, 5], [1, 1, 2, 5],
                                  [2, 1, 0, 7], [2, 1, 1, 7], [2, 1, 2, 7], [2, 1, 3, 7],
-                                 [1, 1, 0, 2]]
+                                 [3, 1, 0, 2]]
     # band (hi, lo): causal diagonal or lk above, -lq below (no windows)
     assert s["hi"].tolist() == [0, 2, 4, 4]
     assert s["lo"].tolist() == [-5, 0, -3, -9]
@@ -61,8 +64,59 @@ def test_aliasing_segments_form_one_kv_group():
                        cap_bwd=100)
     # costs: chunk at offset 4: kv_end = 4+4 = 8 -> 1 tile; offset 12: 16 -> 2 tiles.
     assert s["fwd"].tolist() == [[1, 0], [3, 0], [0, 0], [2, 0]]
-    # two groups of 2 members, cost 3 each -> ascending b_first; 2 kv tiles each
+    # two groups of 2 members, cost 3 each -> ascending first member; 2 kv tiles each
+    assert s["members"].tolist() == [0, 1, 2, 3]
     assert s["bwd"].tolist() == [[0, 2, 0, 16], [0, 2, 1, 16], [2, 2, 0, 16], [2, 2, 1, 16]]
+    assert s["status"] == 0
+
+
+def test_interleaved_chunks_and_a_skipped_member_still_form_one_group():
+    # chunks of documents A (K/V rows 0..15) and B (rows 16..31) in the order
+    # A0, B0, X, A1, B1, where X binds A's rows but has an unknown policy: the
+    # groups are {0, 3} and {1, 4} by their bases, wherever the members sit.
+    prob = _problem([4] * 5, [16] * 5, [1, 1, 9, 1, 1], qco=[4, 4, 4, 12, 12])
+    t = _tensors([0, 4, 8, 12, 16, 20], [0, 16, 0, 0, 16, 32], 20, 32)
+    s = worklist.setup(prob, t, backward=True, bm=4, bn=8, bm_b=4, bn_b=8, cap_fwd=100,
+                       cap_bwd=100)
+    assert s["status"] == oracle.ST_BAD_POLICY
+    assert s["flags"].tolist() == [1, 1, oracle.ST_BAD_POLICY << 8, 1, 1]
+    # backward costs (bm_b = 4, bn_b = 8): offset 4 -> 1 tile, offset 12 -> 2
+    # tiles; both groups cost 3, so the one whose first member is 0 leads
+    assert s["members"].tolist() == [0, 3, 1, 4]
+    assert s["bwd"].tolist() == [[0, 2, 0, 16], [0, 2, 1, 16], [2, 2, 0, 16], [2, 2, 1, 16]]
+    # forward tiles under (bm, bn) = (4, 8): a chunk at offset 12 reaches keys
+    # 0..15 (2 tiles), one at offset 4 keys 0..7 (1 tile); X is not listed
+    assert s["fwd"].tolist() == [[3, 0], [4, 0], [0, 0], [1, 0]]
+
+
+def test_partially_overlapping_kv_groups_are_flagged_and_skipped():
+    # b0 binds key rows 0..7, b1 rows 4..11 (different bases, overlapping
+    # rows), b2 rows 12..15 (disjoint), b3 rows 16..19 and b4 rows 20..23
+    # (touching b3's range, not overlapping it).
+    prob = _problem([2] * 5, [8, 8, 4, 4, 4], [0] * 5)
+    t = _tensors([0, 2, 4, 6, 8, 10], [0, 4, 12, 16, 20, 24], 10, 24)
+    s = worklist.setup(prob, t, backward=True, bm=4, bn=8, bm_b=4, bn_b=8, cap_fwd=100,
+                       cap_bwd=100)
+    ov = oracle.ST_KV_OVERLAP
+    assert s["status"] == ov
+    assert s["flags"].tolist() == [ov << 8, ov << 8, 1, 1, 1]
+    assert s["hi"].tolist()[:2] == [0, 0] and s["lo"].tolist()[:2] == [0, 0]
+    assert s["members"].tolist() == [2, 3, 4]
+    assert s["bwd"][:, 0].tolist() == [0, 1, 2] and s["fwd"][:, 0].tolist() == [2, 3, 4]
+    # a forward setup does not look at key-side outputs at all
+    f = worklist.setup(prob, t, backward=False, bm=4, bn=8, cap_fwd=100)
+    assert f["status"] == 0 and f["fwd"][:, 0].tolist() == [0, 1, 2, 3, 4]
+
+
+def test_same_key_rows_with_different_sources_overlap():
+    # identical dK/dV rows but different K inputs: two groups writing the
+    # same rows
+    prob = _problem([2, 2], [4, 4], [0, 0])
+    t = _tensors([0, 2, 4], [0, 0, 4], 4, 8)
+    t["k"].ragged = np.array([0, 32, 64], np.int64)
+    s = worklist.setup(prob, t, backward=True, bm=4, bn=8, bm_b=4, bn_b=8, cap_fwd=100,
+                       cap_bwd=100)
+    assert s["status"] == oracle.ST_KV_OVERLAP and s["bwd"].shape == (0, 4)
 
 
 def test_invalid_and_overflow():
