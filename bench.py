@@ -145,30 +145,38 @@ def profiled_traffic(kernel: str, workload: str):
 
 def cpu_baseline(batch, target_s: float = 15.0):
     """Time the fp64 oracle's forward, as it stands, on a bounded sample of the
-    same workload: every sequence for the first n query heads, n chosen from a
-    one-head probe so that the timed run takes about `target_s`."""
+    same workload: every sequence for the first n query heads, one head per
+    worker thread on every core this process may run on (BLAS held to one
+    thread per worker, so the workers do not oversubscribe the cores), n
+    chosen from a one-head probe so that the timed run takes about
+    `target_s`."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     prob, t = oracle.from_batch(batch)
     pairs = int(pairs_per_head(batch).sum())
-    t0 = time.perf_counter()
-    oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=[0])
-    probe = time.perf_counter() - t0
-    n = int(max(1, min(batch.h_q, round(target_s / max(probe, 1e-3)))))
-    t0 = time.perf_counter()
-    oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=list(range(n)))
-    spent = time.perf_counter() - t0
+
+    def head(h):
+        oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=[h])
+
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        head(0)
+        probe = time.perf_counter() - t0
+        workers = min(cores, batch.h_q)
+        n = int(max(1, min(batch.h_q, round(target_s * workers / max(probe, 1e-3)))))
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(head, range(n)))
+        spent = time.perf_counter() - t0
     flops = 4.0 * batch.dim * pairs * n
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers),
+            "kind": "oracle", "blas_threads": 1, "host_cores": int(cores),
             "sample": f"fp64 numpy oracle forward over all {batch.batch} sequences for {n} of "
-                      f"{batch.h_q} query heads ({flops / 1e9:.1f} GFLOP causal-aware, "
-                      f"{spent:.1f} s wall)"}
+                      f"{batch.h_q} query heads, one head per thread on {workers} threads "
+                      f"({flops / 1e9:.1f} GFLOP causal-aware, {spent:.1f} s wall)"}
 
 
 def main(argv=None) -> int:

@@ -75,7 +75,10 @@ enum {
                                       aligned */
   VARLEN_ATTN_ERR_STRIDE = 6,      /* 16-bit strides not multiples of 8, or a
                                       stride smaller than one row/head, or
-                                      larger than the span */
+                                      larger than the span, or 127 * stride_t
+                                      + head_dim elements (a 128-row tile)
+                                      reaching 2^31 bytes: tiles are
+                                      addressed with 32-bit byte offsets */
   VARLEN_ATTN_ERR_SPAN = 7,        /* span_elems smaller than one row */
   VARLEN_ATTN_ERR_WORKSPACE = 8,   /* workspace NULL or too small */
   VARLEN_ATTN_ERR_POLICY = 9,      /* default_policy not 0, 1 or 2 */
@@ -114,9 +117,14 @@ enum {
   VARLEN_ATTN_ST_OUT_OF_SPAN = 4,    /* a row of the sequence would reach past
                                         span_elems */
   VARLEN_ATTN_ST_BAD_POLICY = 8,     /* mask_policy[b] not 0, 1 or 2 */
-  VARLEN_ATTN_ST_LIST_OVERFLOW = 16  /* more tiles than the output buffers'
+  VARLEN_ATTN_ST_LIST_OVERFLOW = 16, /* more tiles than the output buffers'
                                         rows can hold (sequences overlap):
                                         nothing is computed */
+  VARLEN_ATTN_ST_KV_OVERLAP = 32     /* backward only: the sequence's dK or dV
+                                        rows intersect those of a sequence
+                                        outside its kv group (see
+                                        varlen_attn_bwd); every sequence of
+                                        both groups is skipped */
 };
 
 /* ---------------------------------------------------------------- types */
@@ -188,9 +196,12 @@ typedef struct varlen_attn_problem {
  *             LSE, dO, dQ, dK, dV
  *   fwd_tiles int32[2 * capacity]: (b, t) for the t-th tile of fwd_block_m
  *             query rows of sequence b
- *   bwd_tiles int32[4 * capacity]: (first b, members, u, max Lk) for the u-th
- *             tile of bwd_block_n key rows of a group of consecutive
- *             sequences that bind the same K, V, dK and dV rows
+ *   bwd_tiles int32[4 * capacity]: (m, members, u, max Lk) for the u-th tile
+ *             of bwd_block_n key rows of a kv group (the sequences that bind
+ *             the same K, V, dK and dV offsets), whose members are
+ *             member_list[m .. m + members)
+ *   members   int32[B] member_list: each kv group's sequences in ascending
+ *             index, groups in the order of bwd_tiles
  *   scratch   setup kernel scratch
  *   delta     fp32 -rowsum(dO * O), same element offsets as LSE (backward
  *             only)
@@ -207,6 +218,7 @@ typedef struct varlen_attn_layout {
   int64_t fwd_tiles_capacity;
   int64_t bwd_tiles_offset;
   int64_t bwd_tiles_capacity;
+  int64_t members_offset;
   int64_t scratch_offset;
   int64_t delta_offset;
   int64_t delta_elems;
@@ -243,25 +255,55 @@ int varlen_attn_bwd_workspace_size(const varlen_attn_problem* p, const varlen_at
 
 /* ---------------------------------------------------------------- compute */
 
-/* Forward.  Reads q, k, v (16-bit); writes o (16-bit) and lse (fp32) for the
- * valid rows of valid sequences only.  `workspace` (device, 256-byte aligned,
- * at least varlen_attn_fwd_workspace_size bytes) is overwritten.
- * `dev_status` (device int32, may be NULL) receives device status bits by
- * atomic OR; the caller clears it.  `stream` is a hipStream_t (NULL: the
- * default stream).  batch == 0 returns VARLEN_ATTN_OK with nothing enqueued.
- * Returns a host code; on nonzero nothing was enqueued. */
+/* Forward.  For every valid sequence b, query head h and row i < Lq(b):
+ *   S = scale * Q_b,h K_b,g(h)^T over the keys visible to the row (the mask
+ *   above), LSE_i = log sum_j exp(S_ij) and O_i = sum_j exp(S_ij - LSE_i) V_j,
+ * i.e. scaled-dot-product attention per sequence, addressed through the bound
+ * per-tensor offsets (cudnn-frontend issue on padded THD, "Concrete failure"
+ * and "Proposal: consume the bound offsets on device"; per-sequence policy in
+ * one launch: TransformerEngine PR #3274, "Description"; LSE as the stats
+ * output with its own offsets and layout: cudnn-frontend PR #462, "What").
+ * Dead rows get O = 0 and LSE = -inf.
+ *   q, k, v    16-bit inputs; read only at valid rows of valid sequences
+ *   o          16-bit output [rows, h_q, D] (any strides)
+ *   lse        fp32 output [rows, h_q] (any strides, e.g. token- or
+ *              head-major)
+ *   workspace  device, 256-byte aligned, at least
+ *              varlen_attn_fwd_workspace_size bytes; overwritten
+ *   dev_status device int32 or NULL: device status bits are ORed in
+ *              (atomic); the caller clears it
+ *   stream     hipStream_t (NULL: the default stream)
+ * Only valid rows of valid sequences are written.  batch == 0 returns
+ * VARLEN_ATTN_OK with nothing enqueued.  Returns a host code; on nonzero
+ * nothing was enqueued.  The caller owns every buffer; the call allocates
+ * nothing and does not synchronise. */
 int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                     const varlen_attn_tensor* o, const varlen_attn_tensor* lse, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream);
 
-/* Backward.  Reads q, k, v, o, dout (16-bit) and lse (fp32, as written by the
- * forward); writes dq, dk, dv (16-bit) for valid rows only.  dK and dV of key
- * rows bound by several consecutive sequences (identical K, V, dK and dV
- * offsets, e.g. context-parallel query chunks of one document) are the sums
- * over those sequences.  Other overlaps between the output rows of different
- * sequences are not allowed and not checked.  Workspace, status and stream as
- * for the forward. */
+/* Backward.  The gradients of sum(dO * O) for the forward above, given dout
+ * (dO) and the forward's o and lse:
+ *   delta_i = sum_d dO_id O_id,  P = exp(S - LSE),  dV = P^T dO,
+ *   dS = P o (dO V^T - delta),   dQ = scale dS K,   dK = scale dS^T Q,
+ * with the stats row-sum intermediate laid out on LSE's own strides and the
+ * workspace sized from every stride axis (cudnn-frontend PR #462, "Root
+ * cause" and "The fix (commit 1)").  Writes dq, dk, dv (16-bit) for valid
+ * rows only.
+ *   kv groups: sequences whose K, V, dK and dV offsets are all identical
+ *   share those key rows (context-parallel query chunks of one document,
+ *   Megatron-LM PR #14, commit message), wherever they sit in the batch;
+ *   their dK and dV are the sums over the group.  A group owns rows
+ *   [0, max Lk) of dK and dV, the element ranges [offset, offset +
+ *   max Lk * stride_t).  When two groups' ranges intersect in dK or in dV,
+ *   every sequence of both groups is skipped (dQ, dK and dV untouched) and
+ *   VARLEN_ATTN_ST_KV_OVERLAP is set: one group's gradients would otherwise
+ *   overwrite the other's without an error (cudnn-frontend issue on padded
+ *   THD, "Concrete failure").  Distinct buffers for dq, dk and dv, and
+ *   disjoint rows between query-side outputs of different sequences, are
+ *   the caller's contract (not checked).
+ * Workspace, status and stream as for the forward; the workspace size comes
+ * from varlen_attn_bwd_workspace_size. */
 int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                     const varlen_attn_tensor* o, const varlen_attn_tensor* dout,
@@ -270,8 +312,11 @@ int varlen_attn_bwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     size_t workspace_bytes, int32_t* dev_status, void* stream);
 
 /* The setup kernel alone, as the forward (varlen_attn_fwd_setup) or the
- * backward (varlen_attn_bwd_setup) runs it first: per-sequence metadata,
- * validity and tile lists in the workspace regions described by
+ * backward (varlen_attn_bwd_setup) runs it first.  It reads the caller's
+ * device offsets, lengths and policies on the device (cudnn-frontend issue on
+ * padded THD, "Proposal: consume the bound offsets on device": one base per
+ * tensor, no device-to-host read) and writes per-sequence metadata, validity,
+ * kv groups and tile lists into the workspace regions described by
  * varlen_attn_layout.  Same arguments and codes as the full calls. */
 int varlen_attn_fwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                           const varlen_attn_tensor* k, const varlen_attn_tensor* v,
@@ -292,12 +337,17 @@ int varlen_attn_bwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor
  * on the same stream, same workspace) wrote there.  The full calls are
  * exactly: varlen_attn_fwd = fwd_setup, fwd_attention;
  * varlen_attn_bwd = bwd_setup, bwd_dq, bwd_dkdv.
- *   fwd_attention    O and LSE of every listed tile
+ *   fwd_attention    O and LSE of every listed tile (the forward's
+ *                    definition above)
  *   bwd_dq           dQ (16-bit), query-major: Q/dO resident, K/V tiles
  *                    streamed; also writes the row terms -delta =
- *                    -rowsum(dO * O) and lse_term (fp32, in the workspace)
+ *                    -rowsum(dO * O) and lse_term (fp32, in the workspace,
+ *                    on LSE's element offsets: cudnn-frontend PR #462,
+ *                    "Root cause")
  *   bwd_dkdv         dK and dV (16-bit), key-major: K/V resident, query tiles
- *                    streamed; reads the row terms, so it follows bwd_dq */
+ *                    of every member of the kv group streamed (Megatron-LM
+ *                    PR #14, commit message); reads the row terms, so it
+ *                    follows bwd_dq */
 int varlen_attn_fwd_attention(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                               const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                               const varlen_attn_tensor* o, const varlen_attn_tensor* lse,

@@ -1,21 +1,23 @@
 """Comparison helpers for the GPU tests (HIP path vs the fp64 oracle)."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 import oracle
 import workloads
 
-# Tolerances (max-abs vs fp64) for the HIP path.  Gradients: 5e-2 absolute,
-# plus 2^-8 of the magnitude, because a bf16 output cannot come closer to the
-# exact value than half an ulp (2^-9 relative) and dS/P enter the bf16 MFMAs
-# rounded the same way; e.g. |dK| = 12 (many queries over few keys) has ulp
-# 0.0625.  For O(1) gradients the bar is the plain 5e-2.
+# Tolerances (max-abs vs fp64) for the HIP path: O 2e-2, dQ/dK/dV 5e-2,
+# LSE 1e-3.  The generators keep gradients O(1) (N(0, 1) inputs, scale
+# 1/sqrt(D), at most four query rows per key row in the random batches), so
+# the gradient bar is the plain absolute one.  One named test covers many
+# queries over few keys, where the gradients themselves grow; its bar is
+# stated there.
 O_TOL = 2e-2
 GRAD_TOL = 5e-2
-GRAD_REL = 2.0 ** -8
 LSE_TOL = 1e-3
 
 
@@ -78,6 +80,50 @@ def oracle_bwd(batch, kv_heads=None):
                            t["dk"], t["dv"], kv_heads=kv_heads)
 
 
+def _workers() -> int:
+    return max(1, min(8, len(os.sched_getaffinity(0))))
+
+
+def _merge(results, names):
+    """One result dict from per-head oracle runs: the written elements of each
+    run, over the first run's buffers."""
+    out = dict(results[0])
+    for n in names:
+        buf, w = out[n].copy(), out[n + "_written"].copy()
+        for r in results[1:]:
+            m = r[n + "_written"]
+            buf[m] = r[n][m]
+            w |= m
+        out[n], out[n + "_written"] = buf, w
+    return out
+
+
+def oracle_fwd_heads(batch, heads):
+    """The oracle forward restricted to `heads` (complete heads: every row of
+    every sequence), one head per worker thread (numpy's products and
+    elementwise kernels release the interpreter lock)."""
+    prob, t = oracle.from_batch(batch)
+
+    def one(h):
+        return oracle.forward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], heads=[h])
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        return _merge(list(ex.map(one, heads)), ("o", "lse"))
+
+
+def oracle_bwd_heads(batch, kv_heads):
+    """The oracle backward restricted to whole GQA groups of `kv_heads`, one
+    kv head per worker thread."""
+    prob, t = oracle.from_batch(batch)
+
+    def one(g):
+        return oracle.backward(prob, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                               t["dk"], t["dv"], kv_heads=[g])
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        return _merge(list(ex.map(one, kv_heads)), ("dq", "dk", "dv"))
+
+
 def check_forward(batch, dev, ref=None, what=""):
     ref = oracle_fwd(batch) if ref is None else ref
     eo = compare_bf16(batch, "o", dev.host("o"), ref["o"], ref["o_written"], O_TOL, what)
@@ -86,10 +132,12 @@ def check_forward(batch, dev, ref=None, what=""):
     return eo, el
 
 
-def check_backward(batch, dev, ref=None, what=""):
+def check_backward(batch, dev, ref=None, what="", rel=0.0):
+    """dQ, dK, dV within GRAD_TOL (+ rel * |ref|) of the oracle; every element
+    outside the written rows untouched."""
     ref = oracle_bwd(batch) if ref is None else ref
     errs = {}
     for n in ("dq", "dk", "dv"):
         errs[n] = compare_bf16(batch, n, dev.host(n), ref[n], ref[n + "_written"], GRAD_TOL, what,
-                               rel=GRAD_REL)
+                               rel=rel)
     return errs

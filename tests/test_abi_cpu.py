@@ -64,6 +64,7 @@ def _fwd(p, q=None, k=None, v=None, o=None, lse=None, ws=FAKE, ws_bytes=1 << 30)
     ("no_offsets", B.ERR_NULL), ("both_offsets", B.ERR_OFFSETS),
     ("multiplier0", B.ERR_OFFSETS), ("multiplier_big", B.ERR_OFFSETS),
     ("window", B.ERR_WINDOW), ("dtype", B.ERR_DTYPE),
+    ("stride_32bit_tile", B.ERR_STRIDE), ("lse_stride_32bit_tile", B.ERR_STRIDE),
 ])
 def test_host_validation_codes(case, code):
     p = _p()
@@ -106,6 +107,16 @@ def test_host_validation_codes(case, code):
         kw["o"] = _t(100 * 512, 512, 128, ragged=None, scaled=FAKE, mult=1 << 31)
     elif case == "dtype":
         p.dtype = 2
+    elif case == "stride_32bit_tile":
+        # a legal-looking row stride whose 128-row tile spans 2^31 bytes: the
+        # kernels' 32-bit buffer offsets would wrap
+        st = ((1 << 30) - 128 + 126) // 127 // 8 * 8 + 8
+        assert (127 * st + 128) * 2 >= 1 << 31
+        kw["k"] = _t(4 * st, st, 128)
+    elif case == "lse_stride_32bit_tile":
+        st = ((1 << 29) - 1 + 126) // 127 + 1
+        assert (127 * st + 1) * 4 >= 1 << 31
+        kw["lse"] = _t(4 * st, st, 1)
     elif case == "window":
         win = (ctypes.c_int32 * 6)(-1, -1, 128, 0, -1, -2)
         p.window_size = ctypes.addressof(win)
@@ -122,6 +133,18 @@ def test_scaled_offsets_pass_host_validation():
     lse = _t(100 * 4, 4, 1, ragged=None, scaled=FAKE, mult=4)
     assert _fwd(_p(), k=k, lse=lse, ws=None) == B.ERR_WORKSPACE
     assert _fwd(_p(batch=0), k=k, lse=lse, ws=None, ws_bytes=0) == B.OK
+
+
+def test_largest_stride_below_the_32bit_tile_limit_passes():
+    """127 * stride_t + D elements of 2 bytes just below 2^31: accepted (the
+    call reaches the workspace check); one multiple of 8 more is refused."""
+    st = ((1 << 30) - 128) // 127 // 8 * 8
+    assert (127 * st + 128) * 2 < 1 << 31
+    assert _fwd(_p(), k=_t(4 * st, st, 128), ws=None) == B.ERR_WORKSPACE
+    big = st + 8
+    while (127 * big + 128) * 2 < 1 << 31:
+        big += 8
+    assert _fwd(_p(), k=_t(4 * big, big, 128), ws=None) == B.ERR_STRIDE
 
 
 def test_window_sizes_pass_host_validation():
@@ -190,7 +213,8 @@ def test_regions_are_disjoint_and_ordered():
                (L.seq_offset, L.seq_i64_offset + 72 * 37),
                (L.fwd_tiles_offset, 8 * L.fwd_tiles_capacity),
                (L.bwd_tiles_offset, 16 * L.bwd_tiles_capacity),
-               (L.scratch_offset, 64 * 37), (L.delta_offset, 4 * L.delta_elems),
+               (L.members_offset, 4 * 37),
+               (L.scratch_offset, 96 * 37), (L.delta_offset, 4 * L.delta_elems),
                (L.lse_term_offset, 4 * L.delta_elems)]
     assert L.seq_i64_offset >= 6 * 4 * 37      # lq, lk, policy, hi, lo, flags
     for (a, n), (b, _) in zip(regions, regions[1:]):

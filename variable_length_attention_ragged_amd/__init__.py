@@ -17,7 +17,7 @@ import torch
 
 from . import _binding as _b
 from ._binding import (CAUSAL_BOTTOM_RIGHT, CAUSAL_TOP_LEFT, PADDING, ST_BAD_OFFSET,
-                       ST_BAD_POLICY, ST_LIST_OVERFLOW, ST_NEG_LENGTH, ST_OUT_OF_SPAN,
+                       ST_BAD_POLICY, ST_KV_OVERLAP, ST_LIST_OVERFLOW, ST_NEG_LENGTH, ST_OUT_OF_SPAN,
                        LibraryMissing, VarlenAttnError, exported_symbols, lib, status_string,
                        varlen_attn_layout, varlen_attn_problem, varlen_attn_tensor)
 
@@ -28,8 +28,8 @@ __all__ = [
     "varlen_attn_bwd_workspace_layout", "varlen_attn_fwd_workspace_size",
     "varlen_attn_bwd_workspace_size", "status_string", "view_span", "PADDING",
     "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "ST_NEG_LENGTH", "ST_BAD_OFFSET",
-    "ST_OUT_OF_SPAN", "ST_BAD_POLICY", "ST_LIST_OVERFLOW", "VarlenAttnError", "LibraryMissing",
-    "lib", "exported_symbols",
+    "ST_OUT_OF_SPAN", "ST_BAD_POLICY", "ST_LIST_OVERFLOW", "ST_KV_OVERLAP", "VarlenAttnError", "LibraryMissing",
+    "lib", "exported_symbols", "VarlenAttention", "varlen_attention",
 ]
 
 
@@ -254,3 +254,86 @@ def _bwd_stage(name):
 
 varlen_attn_bwd_dkdv = _bwd_stage("varlen_attn_bwd_dkdv")
 varlen_attn_bwd_dq = _bwd_stage("varlen_attn_bwd_dq")
+
+
+# ------------------------------------------------------------------ autograd
+
+def _rows_ragged(t: torch.Tensor, rows: torch.Tensor) -> Ragged:
+    """A [rows, heads, dim] (or [rows, heads]) view whose sequences start at
+    the int32 row numbers `rows`: the offsets are formed on the device as
+    rows * stride_t (the library's scaled-offset form)."""
+    return Ragged(t, None, scaled=rows, multiplier=t.stride(0))
+
+
+class VarlenAttention(torch.autograd.Function):
+    """Autograd over varlen_attn_fwd / varlen_attn_bwd.
+
+    forward(q, k, v, problem, rows_q, rows_kv, lse_head_major, status) ->
+    (o, lse).  q: [rows_q, h_q, D], k and v: [rows_kv, h_kv, D] (the
+    problem's dtype, innermost stride 1); rows_q / rows_kv: device int32
+    [batch+1] start rows of the sequences on each side (a padded cu_seqlens).
+    o is a new [rows_q, h_q, D] tensor, lse a new fp32 [rows_q, h_q]
+    (token-major) or a [rows_q, h_q] view of [h_q, rows_q] storage
+    (head-major).  Rows outside every sequence are 0 in o, and their
+    gradients are 0.  lse is not differentiable.  Every number comes from the
+    library's kernels; this class allocates outputs and workspaces and
+    passes pointers."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, problem, rows_q, rows_kv, lse_head_major, status):
+        o = torch.zeros_like(q, memory_format=torch.contiguous_format)
+        if lse_head_major:
+            lse = torch.zeros((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device).t()
+        else:
+            lse = torch.zeros(q.shape[:2], dtype=torch.float32, device=q.device)
+        varlen_attn_fwd(problem, _rows_ragged(q, rows_q), _rows_ragged(k, rows_kv),
+                        _rows_ragged(v, rows_kv), _rows_ragged(o, rows_q),
+                        _rows_ragged(lse, rows_q), dev_status=status)
+        ctx.save_for_backward(q, k, v, o, lse, rows_q, rows_kv)
+        ctx.problem = problem
+        ctx.status = status
+        ctx.mark_non_differentiable(lse)
+        ctx.set_materialize_grads(False)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, grad_o, grad_lse):
+        q, k, v, o, lse, rows_q, rows_kv = ctx.saved_tensors
+        if grad_o is None:
+            return (None,) * 8
+        do = grad_o.contiguous()
+        dq = torch.zeros_like(q, memory_format=torch.contiguous_format)
+        dk = torch.zeros_like(k, memory_format=torch.contiguous_format)
+        dv = torch.zeros_like(v, memory_format=torch.contiguous_format)
+        varlen_attn_bwd(ctx.problem, _rows_ragged(q, rows_q), _rows_ragged(k, rows_kv),
+                        _rows_ragged(v, rows_kv), _rows_ragged(o, rows_q),
+                        _rows_ragged(do, rows_q), _rows_ragged(lse, rows_q),
+                        _rows_ragged(dq, rows_q), _rows_ragged(dk, rows_kv),
+                        _rows_ragged(dv, rows_kv), dev_status=ctx.status)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def varlen_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     cu_seqlens_q: torch.Tensor, cu_seqlens_kv: torch.Tensor, *,
+                     seq_rows_q: torch.Tensor | None = None,
+                     seq_rows_kv: torch.Tensor | None = None,
+                     mask_policy: torch.Tensor | None = None, default_policy: int = PADDING,
+                     q_causal_offset: torch.Tensor | None = None, window_size=None,
+                     scale: float | None = None, lse_head_major: bool = False,
+                     status: torch.Tensor | None = None):
+    """Differentiable ragged attention: returns (o, lse).
+
+    cu_seqlens_q / cu_seqlens_kv: device int32 [batch+1] cumulative valid
+    lengths.  seq_rows_q / seq_rows_kv: device int32 [batch+1] start row of
+    each sequence in q (and o, dO, dQ) and in k, v (and dK, dV), i.e. the
+    padded cu_seqlens; default: the cu_seqlens themselves (packed rows).
+    The other arguments are those of ``Problem``; ``status`` (device int32
+    [1]) receives the device status bits of both passes."""
+    rows_q = cu_seqlens_q if seq_rows_q is None else seq_rows_q
+    rows_kv = cu_seqlens_kv if seq_rows_kv is None else seq_rows_kv
+    for t in (cu_seqlens_q, cu_seqlens_kv, rows_q, rows_kv):
+        if t.dtype != torch.int32:
+            raise TypeError("cu_seqlens and sequence start rows must be int32")
+    problem = Problem(cu_seqlens_q, cu_seqlens_kv, q.shape[1], k.shape[1], q.shape[2], scale,
+                      mask_policy, default_policy, q_causal_offset, window_size, q.dtype)
+    return VarlenAttention.apply(q, k, v, problem, rows_q, rows_kv, lse_head_major, status)

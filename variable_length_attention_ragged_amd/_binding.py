@@ -12,7 +12,9 @@ import os
 from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvarlen_attn.so")
+# VARLEN_ATTN_LIBRARY names another build of the same library (the host-code
+# sanitizer build the CPU tests load); by default the in-tree one.
+LIB_PATH = os.environ.get("VARLEN_ATTN_LIBRARY") or os.path.join(HERE, "libvarlen_attn.so")
 
 # host return codes
 OK = 0
@@ -25,6 +27,7 @@ BF16, F16 = 0, 1
 PADDING, CAUSAL_TOP_LEFT, CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 # device status bits
 ST_NEG_LENGTH, ST_BAD_OFFSET, ST_OUT_OF_SPAN, ST_BAD_POLICY, ST_LIST_OVERFLOW = 1, 2, 4, 8, 16
+ST_KV_OVERLAP = 32
 
 
 class varlen_attn_tensor(ctypes.Structure):
@@ -44,7 +47,7 @@ class varlen_attn_layout(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in (
         "total_bytes", "counters_offset", "header_offset", "seq_offset", "seq_i64_offset",
         "fwd_tiles_offset", "fwd_tiles_capacity", "bwd_tiles_offset", "bwd_tiles_capacity",
-        "scratch_offset", "delta_offset", "delta_elems", "lse_term_offset")] + \
+        "members_offset", "scratch_offset", "delta_offset", "delta_elems", "lse_term_offset")] + \
         [(n, c_int32) for n in ("fwd_block_m", "fwd_block_n", "bwd_block_m", "bwd_block_n")]
 
 

@@ -62,6 +62,11 @@ int check_tensor(const varlen_attn_tensor* t, int heads, int dim, int elem) {
   if (heads > 1 && t->stride_h < dim) return VARLEN_ATTN_ERR_STRIDE;
   if (t->span_elems <= 0) return VARLEN_ATTN_ERR_SPAN;
   if (t->stride_t > t->span_elems || t->stride_h > t->span_elems) return VARLEN_ATTN_ERR_STRIDE;
+  // The kernels address a tile of up to kMaxTileRows rows through one buffer
+  // resource with 32-bit byte offsets from its first row; the largest such
+  // range must stay below 2^31 bytes.
+  if (((int64_t)(kMaxTileRows - 1) * t->stride_t + dim) * elem >= (int64_t(1) << 31))
+    return VARLEN_ATTN_ERR_STRIDE;
   // one row of every head must fit
   const int64_t extra = (int64_t)(heads - 1) * t->stride_h + dim;
   if (extra > t->span_elems) return VARLEN_ATTN_ERR_SPAN;
@@ -108,8 +113,10 @@ void base_layout(int64_t B, int64_t fwd_cap, int64_t bwd_cap, varlen_attn_layout
   L->bwd_tiles_offset = off;
   L->bwd_tiles_capacity = bwd_cap;
   off += align256(bwd_cap * 16);
+  L->members_offset = off;
+  off += align256(4 * B);
   L->scratch_offset = off;
-  off += align256(64 * B);
+  off += align256((int64_t)kSetupScratchPerSeq * B);
   L->delta_offset = off;
   L->lse_term_offset = off;
   L->total_bytes = off;
@@ -133,6 +140,7 @@ WsView make_view(char* ws, const varlen_attn_layout& L, int64_t B) {
   w.base = (int64_t*)(ws + L.seq_offset + L.seq_i64_offset);
   w.fwd_tiles = (int32_t*)(ws + L.fwd_tiles_offset);
   w.bwd_tiles = (int32_t*)(ws + L.bwd_tiles_offset);
+  w.members = (int32_t*)(ws + L.members_offset);
   w.scratch = ws + L.scratch_offset;
   w.delta = (float*)(ws + L.delta_offset);
   w.lse_term = (float*)(ws + L.lse_term_offset);
@@ -457,7 +465,9 @@ const char* varlen_attn_status_string(int code) {
     case VARLEN_ATTN_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
     case VARLEN_ATTN_ERR_HEADS: return "h_q and h_kv must be >= 1 with h_q % h_kv == 0";
     case VARLEN_ATTN_ERR_ALIGN: return "misaligned pointer (bf16 data 16 B, LSE 4 B, workspace 256 B)";
-    case VARLEN_ATTN_ERR_STRIDE: return "invalid stride (bf16 strides multiples of 8, >= one row/head, <= span)";
+    case VARLEN_ATTN_ERR_STRIDE:
+      return "invalid stride (16-bit strides multiples of 8, >= one row/head, <= span, and "
+             "128 rows of stride_t within 2^31 bytes)";
     case VARLEN_ATTN_ERR_SPAN: return "span_elems smaller than one row of every head";
     case VARLEN_ATTN_ERR_WORKSPACE: return "workspace missing or smaller than the required size";
     case VARLEN_ATTN_ERR_POLICY: return "default_policy must be 0, 1 or 2";

@@ -11,8 +11,8 @@
 //   dkdv         one item = (kv group, 128-key tile, kv head).  Each wave keeps
 //                32 keys of K and V in registers; 64-row query tiles of every
 //                query head of the GQA group and every member sequence of the
-//                kv group (sequences binding the same K/V rows) stream through
-//                LDS, double-buffered:
+//                kv group (sequences binding the same K/V rows, listed by the
+//                setup kernel) stream through LDS, double-buffered:
 //                  S = Q K^T, P = exp(S*scale - LSE) (0 where masked or dead),
 //                  dP = dO V^T, dS = P o (dP - delta),
 //                  dV += P^T dO, dK += dS^T Q   (dO and Q read transposed);
@@ -68,7 +68,11 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   const int B = a.batch;
   const WsView& w = a.ws;
 
-  const int bfirst = ldm(entry + 0), members = ldm(entry + 1), u = ldm(entry + 2), lmax = ldm(entry + 3);
+  // the group's members are w.members[mstart .. mstart + members): sequences
+  // that bind the same K, V, dK and dV rows
+  const int mstart = ldm(entry + 0), members = ldm(entry + 1), u = ldm(entry + 2), lmax = ldm(entry + 3);
+  const int32_t* mlist = w.members + mstart;
+  const int bfirst = ldm(mlist);
   const int k0 = u * BN;
   const int wk0 = k0 + wave * 32;
   const int my_key = wk0 + l32;
@@ -103,7 +107,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   // sequences, BM-row tiles over the rows whose band reaches keys
   // k0 .. k0+BN-1: rows k0 - hi .. k0 + BN - 1 - lo.
   auto row_range = [&](int mi, int& qs, int& end) -> bool {
-    const int b = bfirst + mi;
+    const int b = ldm(mlist + mi);
     const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
     if (lq <= 0 || lk <= k0) return false;
     const int64_t first = max((int64_t)k0 - ldm(w.hi + b), (int64_t)0);
@@ -132,7 +136,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
     return seek(p);
   };
   auto issue = [&](const QPos& p, int buf) {
-    const int b = bfirst + p.mi, h = g * a.group + p.hh;
+    const int b = ldm(mlist + p.mi), h = g * a.group + p.hh;
     const int nrows = min(BM, ldm(w.lq + b) - p.qs);
     const int64_t qs = p.qs;
     issue_tile<D, BM>(a.q + ldm(w.base + (T_Q * B + b)) + qs * a.q_st + (int64_t)h * a.q_sh, nrows, a.q_st,
@@ -291,7 +295,7 @@ __device__ void dkdv_item(const BwdArgs& a, const DkdvSmem<D> sm, const int32_t*
   auto step = [&](auto BUF) {
     constexpr int buf = decltype(BUF)::value;
     const QPos nx = next(cur);
-    const int b = bfirst + cur.mi;
+    const int b = ldm(mlist + cur.mi);
     const int lq = ldm(w.lq + b), lk = ldm(w.lk + b);
     const int qs = cur.qs;
     wait_tile_loads();
@@ -608,8 +612,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 }  // namespace
-
-constexpr int kFlatGrid = 4096;
 
 template <int D, class T>
 void launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {

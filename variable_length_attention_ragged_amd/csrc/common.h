@@ -15,9 +15,13 @@ constexpr int kFwdBlockM = 128;
 constexpr int kFwdBlockN = 64;
 constexpr int kBwdBlockM = 64;
 constexpr int kBwdBlockN = 128;
-constexpr int kQueues = 8;        // one claim queue per XCD (8 XCDs on MI355X)
+constexpr int kQueues = 8;
+// Rows of the largest tile any kernel addresses from one buffer resource
+// with 32-bit byte offsets (query tiles; 64-entry LSE columns are smaller).
+constexpr int kMaxTileRows = 128;        // one claim queue per XCD (8 XCDs on MI355X)
 constexpr float kLog2eHost = 1.4426950408889634f;
 constexpr int kCounterWords = 64;
+constexpr int kSetupScratchPerSeq = 96;  // bytes of setup scratch per sequence
 
 enum TensorId { T_Q = 0, T_K, T_V, T_O, T_LSE, T_DO, T_DQ, T_DK, T_DV, T_COUNT };
 
@@ -61,7 +65,8 @@ struct WsView {
   int32_t* flags;
   int64_t* base;        // [T_COUNT][batch]
   int32_t* fwd_tiles;   // (b, t) pairs
-  int32_t* bwd_tiles;   // (first, members, u, max_lk) quadruples
+  int32_t* bwd_tiles;   // (member-list start, members, u, max_lk) quadruples
+  int32_t* members;     // each kv group's members, groups in list order
   char* scratch;
   float* delta;       // -rowsum(dO * O) at LSE's element offsets
   float* lse_term;    // -LSE * log2(e) / c at LSE's element offsets

@@ -14,9 +14,9 @@
 //
 // Ordering (this library's design): sequences by descending cost, ties by
 // index; a sequence's query tiles from last to first (causal tiles late in a
-// sequence see the most keys).  kv groups (consecutive sequences binding the
-// same K, V, dK, dV rows) likewise by descending cost.  Everything is integer
-// arithmetic and deterministic.
+// sequence see the most keys).  kv groups (sequences binding the same K, V,
+// dK, dV rows) likewise by descending cost, ties by first member.
+// Everything is integer arithmetic and deterministic.
 #include "common.h"
 
 namespace vattn {
@@ -124,10 +124,10 @@ __device__ int64_t block_exclusive_scan(int n, F value, int32_t* out) {
 }
 
 // L: the batch fits kLdsSeq, and the per-sequence state every phase reads
-// back (lengths, flags, costs, orders, positions, kv-group tables) lives in
-// LDS instead of the workspace scratch, so the phases chain through LDS
-// rather than through dependent global-memory round trips.  The outputs are
-// written to the workspace either way.
+// back (lengths, flags, costs, orders, positions, kv-group tables, the
+// key-side bases) lives in LDS instead of the workspace scratch, so the
+// phases chain through LDS rather than through dependent global-memory round
+// trips.  The outputs are written to the workspace either way.
 template <bool L>
 __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   const int tid = threadIdx.x;
@@ -135,22 +135,25 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   const WsView& w = a.ws;
   __shared__ int s_status;
   __shared__ int s_listed;
-  __shared__ int s_groups;
+  __shared__ int s_kept;
   if (tid == 0) {
     s_status = 0;
     s_listed = 0;
-    s_groups = 0;
+    s_kept = 0;
   }
   for (int i = tid; i < kCounterWords; i += kSetupThreads) w.counters[i] = 0;
 
-  // Scratch (64 bytes per sequence): int64 cost_f[B], cost_b[B], gcost[B];
-  // int32 order[B], pos[B], gfirst[B], gsize[B], glmax[B], gorder[B], gpos[B],
-  // gidx[B], same[B] (K, V, dK, dV bases equal those of b-1).  In LDS when L,
-  // together with copies of lq, lk and flags.
+  // Scratch (kSetupScratchPerSeq bytes per sequence): int64 cost_f[B],
+  // cost_b[B], gcost[B]; int32 order[B], pos[B], gfirst[B], gsize[B],
+  // glmax[B], gorder[B], gpos[B], gidx[B], rep[B], clash[B], gmpos[B].  In
+  // LDS when L, together with copies of lq, lk, flags, hi, lo and of the K,
+  // V, dK, dV bases.
   constexpr int NL = L ? kLdsSeq : 1;
   __shared__ int64_t s_cost[3][NL];
-  __shared__ int32_t s_idx[9][NL];
+  __shared__ int32_t s_idx[11][NL];
   __shared__ int32_t s_meta[5][NL];  // lq, lk, flags, hi, lo
+  __shared__ int64_t s_base[4][NL];  // K, V, dK, dV
+  static_assert(3 * 8 + 11 * 4 <= kSetupScratchPerSeq, "setup scratch too small");
   int64_t* const gscratch = (int64_t*)w.scratch;
   int32_t* const iscratch = (int32_t*)(gscratch + 3 * (int64_t)B);
   int64_t* cost_f = L ? s_cost[0] : gscratch;
@@ -164,11 +167,19 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   int32_t* gorder = L ? s_idx[5] : iscratch + 5 * (int64_t)B;
   int32_t* gpos = L ? s_idx[6] : iscratch + 6 * (int64_t)B;
   int32_t* gidx = L ? s_idx[7] : iscratch + 7 * (int64_t)B;
-  int32_t* same = L ? s_idx[8] : iscratch + 8 * (int64_t)B;
+  int32_t* rep = L ? s_idx[8] : iscratch + 8 * (int64_t)B;
+  int32_t* clash = L ? s_idx[9] : iscratch + 9 * (int64_t)B;
+  int32_t* gmpos = L ? s_idx[10] : iscratch + 10 * (int64_t)B;
   // lq, lk, flags as read back by the later phases
-  const int32_t* m_lq = L ? s_meta[0] : w.lq;
-  const int32_t* m_lk = L ? s_meta[1] : w.lk;
-  const int32_t* m_flags = L ? s_meta[2] : w.flags;
+  int32_t* m_lq = L ? s_meta[0] : w.lq;
+  int32_t* m_lk = L ? s_meta[1] : w.lk;
+  int32_t* m_flags = L ? s_meta[2] : w.flags;
+  // key-side bases: K, V, dK, dV of sequence b at kv_base[i][b]
+  const int64_t* kv_base[4];
+  {
+    const int ids[4] = {T_K, T_V, T_DK, T_DV};
+    for (int i = 0; i < 4; ++i) kv_base[i] = L ? s_base[i] : w.base + (int64_t)ids[i] * B;
+  }
   __syncthreads();
 
   // ---- per-sequence metadata and validation
@@ -225,17 +236,15 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     }
     for (int id = 0; id < T_COUNT; ++id)
       w.base[(int64_t)id * B + b] = a.t[id].present ? offset_of(a.t[id], b) : 0;
-    // does b bind the K, V, dK and dV rows of b-1 (one kv group)?
-    bool same_kv = b > 0;
-    for (int id : {(int)T_K, (int)T_V, (int)T_DK, (int)T_DV})
-      if (same_kv && a.t[id].present) same_kv = offset_of(a.t[id], b) == offset_of(a.t[id], b - 1);
-    same[b] = same_kv ? 1 : 0;
+    if (L) {
+      const int ids[4] = {T_K, T_V, T_DK, T_DV};
+      for (int i = 0; i < 4; ++i) s_base[i][b] = a.t[ids[i]].present ? offset_of(a.t[ids[i]], b) : 0;
+    }
     if (!L) {
       cost_f[b] = (valid && lq > 0) ? sequence_cost(lq, lk, hi, lo, a.bm, a.bn) : 0;
       cost_b[b] = (valid && a.backward) ? sequence_cost(lq, lk, hi, lo, a.bm_b, a.bn_b) : 0;
     }
     if (st) atomicOr(&s_status, st);
-    if (valid && lq > 0) atomicAdd(&s_listed, 1);
   }
   __syncthreads();
   if (L) {
@@ -255,12 +264,94 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
     __syncthreads();
   }
 
-  // ---- forward tile list: rank listed sequences by (cost desc, index asc).
-  //      Sort key: the cost of a listed sequence, -1 for the others.
   __shared__ int64_t s_key[kLdsSeq];
   __shared__ int32_t s_first[kLdsSeq];
+
+  // ---- backward kv groups: valid sequences with key rows whose K, V, dK
+  //      and dV bases all agree form one group, wherever they sit in the
+  //      batch (context-parallel query chunks of one document).  A group owns
+  //      rows [0, max Lk) of its dK and dV tensors; groups whose rows
+  //      intersect in either would overwrite each other's gradients, so all
+  //      their members are dropped with ST_KV_OVERLAP before any list is
+  //      written.
+  int n_groups = 0;
+  if (a.backward) {
+    auto member = [&](int b) { return (m_flags[b] & 1) && m_lk[b] > 0; };
+    auto same_key = [&](int x, int y) {
+      return kv_base[2][x] == kv_base[2][y] && kv_base[3][x] == kv_base[3][y] &&
+             kv_base[0][x] == kv_base[0][y] && kv_base[1][x] == kv_base[1][y];
+    };
+    // the group's representative: its first member
+    for (int b = tid; b < B; b += kSetupThreads) {
+      int r = -1;
+      if (member(b))
+        for (int o = 0; o <= b; ++o)
+          if (member(o) && same_key(o, b)) {
+            r = o;
+            break;
+          }
+      rep[b] = r;
+    }
+    __syncthreads();
+    n_groups = (int)block_exclusive_scan(
+        B, [&](int b) { return (int64_t)(rep[b] == b ? 1 : 0); }, gidx);
+    for (int b = tid; b < B; b += kSetupThreads) {
+      if (rep[b] != b) continue;
+      const int g = gidx[b];
+      int n = 0, lmax = 0;
+      int64_t c = 0;
+      for (int o = b; o < B; ++o)
+        if (rep[o] == b) {
+          ++n;
+          lmax = max(lmax, (int)m_lk[o]);
+          c += cost_b[o];
+        }
+      gfirst[g] = b;
+      gsize[g] = n;
+      glmax[g] = lmax;
+      gcost[g] = c;
+    }
+    __syncthreads();
+    // row ranges [base, base + lmax * stride_t) of dK and dV, pairwise
+    const int64_t st_dk = a.t[T_DK].st, st_dv = a.t[T_DV].st;
+    for (int g = tid; g < n_groups; g += kSetupThreads) {
+      const int f = gfirst[g];
+      const int64_t k0 = kv_base[2][f], k1 = k0 + (int64_t)glmax[g] * st_dk;
+      const int64_t v0 = kv_base[3][f], v1 = v0 + (int64_t)glmax[g] * st_dv;
+      int hit = 0;
+      for (int o = 0; o < n_groups && !hit; ++o) {
+        if (o == g) continue;
+        const int fo = gfirst[o];
+        const int64_t ok0 = kv_base[2][fo], ok1 = ok0 + (int64_t)glmax[o] * st_dk;
+        const int64_t ov0 = kv_base[3][fo], ov1 = ov0 + (int64_t)glmax[o] * st_dv;
+        hit = (k0 < ok1 && ok0 < k1) || (v0 < ov1 && ov0 < v1);
+      }
+      clash[g] = hit;
+      if (!hit) atomicAdd(&s_kept, 1);
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += kSetupThreads) {
+      if (rep[b] < 0 || !clash[gidx[rep[b]]]) continue;
+      const int st = VARLEN_ATTN_ST_KV_OVERLAP;
+      w.flags[b] = st << 8;
+      w.hi[b] = 0;
+      w.lo[b] = 0;
+      if (L) {
+        s_meta[2][b] = st << 8;
+        s_meta[3][b] = 0;
+        s_meta[4][b] = 0;
+      }
+      atomicOr(&s_status, st);
+    }
+    __syncthreads();
+  }
+
+  // ---- forward tile list: rank listed sequences by (cost desc, index asc).
+  //      Sort key: the cost of a listed sequence, -1 for the others.
   const bool in_lds = B <= kLdsSeq;
   auto listed = [&](int b) { return (m_flags[b] & 1) && m_lq[b] > 0; };
+  for (int b = tid; b < B; b += kSetupThreads)
+    if (listed(b)) atomicAdd(&s_listed, 1);
   if (in_lds)
     for (int b = tid; b < B; b += kSetupThreads) s_key[b] = listed(b) ? cost_f[b] : -1;
   __syncthreads();
@@ -285,41 +376,21 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
   const int64_t n_fwd = block_exclusive_scan(
       n_listed, [&](int r) { return ceil_div64(m_lq[order[r]], bm); }, pos);
 
-  // ---- backward kv groups
+  // ---- backward kv-tile list: the kept groups by (cost desc, first member
+  //      asc); tile positions and member-list positions by scans in that order
   int64_t n_bwd = 0;
-  int n_groups = 0;
+  int n_kept = 0;
   if (a.backward) {
-    auto member = [&](int b) { return (m_flags[b] & 1) && m_lk[b] > 0; };
-    auto starts = [&](int b) { return member(b) && !(b > 0 && member(b - 1) && same[b]); };
-    // group index of each group start = number of starts before it
-    const int64_t total_starts =
-        block_exclusive_scan(B, [&](int b) { return (int64_t)(starts(b) ? 1 : 0); }, gidx);
-    for (int b = tid; b < B; b += kSetupThreads) {
-      if (!starts(b)) continue;
-      const int g = gidx[b];
-      int n = 1;
-      int lmax = m_lk[b];
-      int64_t c = cost_b[b];
-      while (b + n < B && member(b + n) && same[b + n]) {
-        lmax = max(lmax, m_lk[b + n]);
-        c += cost_b[b + n];
-        ++n;
-      }
-      gfirst[g] = b;
-      gsize[g] = n;
-      glmax[g] = lmax;
-      gcost[g] = c;
-    }
-    n_groups = (int)total_starts;
-    __syncthreads();
+    n_kept = s_kept;
     const bool g_in_lds = n_groups <= kLdsSeq;
     if (g_in_lds)
       for (int g = tid; g < n_groups; g += kSetupThreads) {
-        s_key[g] = gcost[g];
+        s_key[g] = clash[g] ? -1 : gcost[g];
         s_first[g] = gfirst[g];
       }
     __syncthreads();
     for (int g = tid; g < n_groups; g += kSetupThreads) {
+      if (clash[g]) continue;
       const int64_t cg = gcost[g];
       const int fg = gfirst[g];
       int r = 0;
@@ -330,14 +401,15 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
         }
       } else {
         for (int o = 0; o < n_groups; ++o)
-          if (gcost[o] > cg || (gcost[o] == cg && gfirst[o] < fg)) ++r;
+          if (!clash[o] && (gcost[o] > cg || (gcost[o] == cg && gfirst[o] < fg))) ++r;
       }
       gorder[r] = g;
     }
     __syncthreads();
     const int bn_b = a.bn_b;
     n_bwd = block_exclusive_scan(
-        n_groups, [&](int r) { return ceil_div64(glmax[gorder[r]], bn_b); }, gpos);
+        n_kept, [&](int r) { return ceil_div64(glmax[gorder[r]], bn_b); }, gpos);
+    block_exclusive_scan(n_kept, [&](int r) { return (int64_t)gsize[gorder[r]]; }, gmpos);
   }
 
   // ---- capacity check, then write the lists
@@ -353,16 +425,20 @@ __global__ __launch_bounds__(kSetupThreads) void setup_kernel(SetupArgs a) {
       }
     }
     if (a.backward) {
-      for (int r = tid; r < n_groups; r += kSetupThreads) {
+      for (int r = tid; r < n_kept; r += kSetupThreads) {
         const int g = gorder[r];
         const int nt = (int)ceil_div64(glmax[g], a.bn_b);
         int32_t* dst = w.bwd_tiles + 4 * (int64_t)gpos[r];
         for (int u = 0; u < nt; ++u) {
-          dst[4 * u] = gfirst[g];
+          dst[4 * u] = gmpos[r];
           dst[4 * u + 1] = gsize[g];
           dst[4 * u + 2] = u;
           dst[4 * u + 3] = glmax[g];
         }
+        int32_t* mem = w.members + gmpos[r];
+        const int f = gfirst[g];
+        for (int o = f, k = 0; o < B && k < gsize[g]; ++o)
+          if (rep[o] == f) mem[k++] = o;
       }
     }
   }

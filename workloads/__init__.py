@@ -300,8 +300,9 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
                  q_causal_offset: bool = False, lse_kind: str | None = None,
                  zero_lengths: bool = True, with_grad: bool = True,
                  window=None, dtype: str = "bf16") -> Batch:
-    """A small random ragged batch for parity tests: random lengths (some 0),
-    random row gaps between sequences (separately for the query-side and
+    """A small random ragged batch for parity tests: random lengths (some 0;
+    a nonzero key length is at least a quarter of the query length), random
+    row gaps between sequences (separately for the query-side and
     key-side buffers), random per-tensor token-stride gaps n*H*D (n = 0..3),
     random per-sequence policies and LSE layout.  ``window``: None, an int32
     [3, 2] array of per-policy (left, right) windows, or "random" (each side
@@ -310,6 +311,9 @@ def random_batch(seed: int, *, batch: int = 4, max_len: int = 200, h_q: int = 4,
     lo = 0 if zero_lengths else 1
     lq = rng.integers(lo, max_len, size=batch, endpoint=True)
     lk = rng.integers(lo, max_len, size=batch, endpoint=True) if cross else lq.copy()
+    # at most four query rows per key row, so that no key gathers the
+    # gradients of many queries (gradients stay O(1))
+    lk = np.where(lk > 0, np.maximum(lk, (lq + 3) // 4), lk)
     lead_q, lead_k = rng.integers(0, max_gap + 1, size=2)
     gq = rng.integers(0, max_gap, size=batch, endpoint=True)
     gk = rng.integers(0, max_gap, size=batch, endpoint=True)

@@ -22,11 +22,17 @@ class DeviceBatch:
     on one side (query or key) whose rows start at the same numbers share one
     row array."""
 
+    GUARD_BITS = 0x5AA5   # canary pattern of the guard bands (16-bit words)
+
     def __init__(self, batch: Batch, device="cuda", with_grad: bool | None = None,
-                 scaled_offsets: bool = False):
+                 scaled_offsets: bool = False, guard_elems: int = 0):
         self.batch = batch
         self.device = device
         self.scaled_offsets = scaled_offsets
+        # guard_elems > 0: every output buffer sits between two bands of that
+        # many elements holding GUARD_BITS (see guards_intact)
+        self.guard_elems = guard_elems
+        self.guarded = {}
         with_grad = ("do" in batch.data) if with_grad is None else with_grad
         self.flat = {}
         for n in ("q", "k", "v", "do"):
@@ -61,11 +67,31 @@ class DeviceBatch:
 
     def fresh_output(self, n: str) -> torch.Tensor:
         lay = self.batch.layouts[n]
+        g = self.guard_elems
         if n == "lse":
-            return torch.full((lay.span,), F32_OUT_NAN, dtype=torch.int32,
-                              device=self.device).view(torch.float32)
-        return torch.full((lay.span,), OUT_NAN[self.batch.dtype], dtype=torch.int16,
-                          device=self.device).view(TORCH_DTYPE[self.batch.dtype])
+            buf = torch.full((lay.span + 2 * g,), (self.GUARD_BITS << 16) | self.GUARD_BITS,
+                             dtype=torch.int32, device=self.device)
+            buf[g:g + lay.span] = F32_OUT_NAN - (1 << 32) if F32_OUT_NAN >= 1 << 31 else F32_OUT_NAN
+            self.guarded[n] = buf
+            return buf[g:g + lay.span].view(torch.float32)
+        buf = torch.full((lay.span + 2 * g,), self.GUARD_BITS, dtype=torch.int16,
+                         device=self.device)
+        out = OUT_NAN[self.batch.dtype]
+        buf[g:g + lay.span] = out - (1 << 16) if out >= 1 << 15 else out
+        self.guarded[n] = buf
+        return buf[g:g + lay.span].view(TORCH_DTYPE[self.batch.dtype])
+
+    def guards_intact(self) -> dict:
+        """Per output buffer: True if both guard bands still hold the canary."""
+        g = self.guard_elems
+        res = {}
+        for n, buf in self.guarded.items():
+            h = buf.cpu().numpy()
+            word = (self.GUARD_BITS << 16) | self.GUARD_BITS if n == "lse" else self.GUARD_BITS
+            band = np.concatenate([h[:g], h[h.size - g:]]).view(
+                np.uint32 if n == "lse" else np.uint16)
+            res[n] = bool(np.all(band == word))
+        return res
 
     def rag(self, n: str) -> va.Ragged:
         lay = self.batch.layouts[n]
