@@ -88,8 +88,14 @@ enum {
                                       `ragged_scaled`, or ragged_multiplier is
                                       outside [1, 2^31) */
   VARLEN_ATTN_ERR_WINDOW = 13,     /* a window_size entry below -1 */
-  VARLEN_ATTN_ERR_DTYPE = 14       /* dtype not VARLEN_ATTN_BF16 or _F16 */
+  VARLEN_ATTN_ERR_DTYPE = 14,      /* dtype not VARLEN_ATTN_BF16 or _F16 */
+  VARLEN_ATTN_ERR_SCRATCH = 15     /* varlen_attn_fwd_noalloc: the forward
+                                      workspace this problem needs exceeds
+                                      VARLEN_ATTN_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the static per-GPU workspace of varlen_attn_fwd_noalloc. */
+#define VARLEN_ATTN_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Element types of the 16-bit tensors. */
 enum {
@@ -281,6 +287,25 @@ int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                     const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                     const varlen_attn_tensor* o, const varlen_attn_tensor* lse, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/* Forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments (minus the workspace), results and
+ * host codes as varlen_attn_fwd, whose kernels it runs.  Its workspace is a
+ * static array of VARLEN_ATTN_NOALLOC_SCRATCH_BYTES (4 MiB) that the library
+ * holds on each GPU it runs on until the process ends; a problem whose
+ * varlen_attn_fwd_workspace_size exceeds it returns VARLEN_ATTN_ERR_SCRATCH
+ * with nothing enqueued (the size grows with the batch and the output rows:
+ * about 204 bytes per sequence plus 8 bytes per 128 rows of o).  Nothing is
+ * allocated: the array's device address is looked up once per device, at the
+ * first call with that device current.  All calls on one GPU share the
+ * array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must not be issued; calls in order on one stream are
+ * fine. */
+int varlen_attn_fwd_noalloc(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                            const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                            const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
+                            int32_t* dev_status, void* stream);
 
 /* Backward.  The gradients of sum(dO * O) for the forward above, given dout
  * (dO) and the forward's o and lse:

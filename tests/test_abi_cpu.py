@@ -232,3 +232,33 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("oracles", ""), f
+
+
+def _fwd_noalloc(p, **kw):
+    d = p.head_dim
+    q = kw.get("q") or _t(100 * p.h_q * d, p.h_q * d, d)
+    k = kw.get("k") or _t(100 * p.h_kv * d, p.h_kv * d, d)
+    v = kw.get("v") or _t(100 * p.h_kv * d, p.h_kv * d, d)
+    o = kw.get("o") or _t(100 * p.h_q * d, p.h_q * d, d)
+    lse = kw.get("lse") or _t(100 * p.h_q, p.h_q, 1)
+    return va.lib().varlen_attn_fwd_noalloc(ctypes.byref(p), ctypes.byref(q), ctypes.byref(k),
+                                            ctypes.byref(v), ctypes.byref(o), ctypes.byref(lse),
+                                            None, None)
+
+
+def test_noalloc_forward_host_checks():
+    """The workspace-free forward applies the forward's host checks, refuses a
+    problem whose workspace exceeds its static 4 MiB with ERR_SCRATCH before
+    touching the device, and returns OK for an empty batch."""
+    assert _fwd_noalloc(_p(d=96)) == B.ERR_HEAD_DIM
+    assert _fwd_noalloc(_p(), q=_t(100 * 512, 512, 128, data=FAKE + 8)) == B.ERR_ALIGN
+    assert _fwd_noalloc(_p(batch=0)) == B.OK
+    # about 204 bytes per sequence: 30000 sequences need more than 4 MiB
+    big = _p(batch=30000)
+    size = ctypes.c_size_t(0)
+    o = _t(100 * 512, 512, 128)
+    assert va.lib().varlen_attn_fwd_workspace_size(ctypes.byref(big), ctypes.byref(o),
+                                                   ctypes.byref(size)) == B.OK
+    assert size.value > B.NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(big) == B.ERR_SCRATCH
+    assert "static scratch" in va.status_string(B.ERR_SCRATCH)

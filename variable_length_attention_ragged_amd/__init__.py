@@ -29,7 +29,7 @@ __all__ = [
     "varlen_attn_bwd_workspace_size", "status_string", "view_span", "PADDING",
     "CAUSAL_TOP_LEFT", "CAUSAL_BOTTOM_RIGHT", "ST_NEG_LENGTH", "ST_BAD_OFFSET",
     "ST_OUT_OF_SPAN", "ST_BAD_POLICY", "ST_LIST_OVERFLOW", "ST_KV_OVERLAP", "VarlenAttnError", "LibraryMissing",
-    "lib", "exported_symbols", "VarlenAttention", "varlen_attention",
+    "lib", "exported_symbols", "VarlenAttention", "varlen_attention", "varlen_attn_fwd_noalloc",
 ]
 
 
@@ -193,6 +193,20 @@ def varlen_attn_fwd(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged, lse:
     (allocated with torch if not given).  Raises VarlenAttnError on a host
     error code (nothing enqueued)."""
     return _fwd_call("varlen_attn_fwd", p, q, k, v, o, lse, workspace, dev_status, stream)
+
+
+def varlen_attn_fwd_noalloc(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged,
+                            lse: Ragged, *, dev_status: torch.Tensor | None = None,
+                            stream=None) -> None:
+    """Enqueue the forward with the library's static per-GPU workspace instead
+    of a workspace argument: nothing is allocated, here or in the library.
+    Raises VarlenAttnError (code ERR_SCRATCH) if the problem needs more than
+    that workspace holds."""
+    _check_dtypes(p, (q, k, v, o), lse)
+    code = lib().varlen_attn_fwd_noalloc(
+        ctypes.byref(p.c()), ctypes.byref(q.c()), ctypes.byref(k.c()), ctypes.byref(v.c()),
+        ctypes.byref(o.c()), ctypes.byref(lse.c()), _ptr(dev_status), _stream(stream))
+    _b._check(code, "varlen_attn_fwd_noalloc")
 
 
 def varlen_attn_fwd_setup(p: Problem, q: Ragged, k: Ragged, v: Ragged, o: Ragged, lse: Ragged,

@@ -20,7 +20,8 @@ LIB_PATH = os.environ.get("VARLEN_ATTN_LIBRARY") or os.path.join(HERE, "libvarle
 OK = 0
 ERR_NULL, ERR_BATCH, ERR_HEAD_DIM, ERR_HEADS, ERR_ALIGN, ERR_STRIDE = 1, 2, 3, 4, 5, 6
 ERR_SPAN, ERR_WORKSPACE, ERR_POLICY, ERR_SCALE, ERR_HIP = 7, 8, 9, 10, 11
-ERR_OFFSETS, ERR_WINDOW, ERR_DTYPE = 12, 13, 14
+ERR_OFFSETS, ERR_WINDOW, ERR_DTYPE, ERR_SCRATCH = 12, 13, 14, 15
+NOALLOC_SCRATCH_BYTES = 4 << 20
 # element types of the 16-bit tensors
 BF16, F16 = 0, 1
 # mask policies
@@ -74,6 +75,7 @@ _SIGNATURES = {
     "varlen_attn_bwd_workspace_size": [_P, _T, _T, _T, POINTER(c_size_t)],
     "varlen_attn_fwd": [_P, _T, _T, _T, _T, _T, c_void_p, c_size_t, c_void_p, c_void_p],
     "varlen_attn_fwd_setup": [_P, _T, _T, _T, _T, _T, c_void_p, c_size_t, c_void_p, c_void_p],
+    "varlen_attn_fwd_noalloc": [_P, _T, _T, _T, _T, _T, c_void_p, c_void_p],
     "varlen_attn_bwd": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t, c_void_p,
                         c_void_p],
     "varlen_attn_bwd_setup": [_P, _T, _T, _T, _T, _T, _T, _T, _T, _T, c_void_p, c_size_t,

@@ -13,6 +13,14 @@
 
 #include "common.h"
 
+// Workspace of varlen_attn_fwd_noalloc: one array per GPU, holding the
+// forward's metadata, tile list, counters and setup scratch for callers that
+// cannot allocate.  Host code never passes this name to a kernel (on the host
+// it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 namespace vattn {
 
 int persistent_grid(const void* kernel, int threads, size_t lds_bytes) {
@@ -39,6 +47,22 @@ int persistent_grid(const void* kernel, int threads, size_t lds_bytes) {
   std::lock_guard<std::mutex> g(mu);
   cache[key] = grid;
   return grid;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current and kept; nullptr if the lookup fails.
+static void* noalloc_scratch() {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) return it->second;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  addr[dev] = ptr;
+  return ptr;
 }
 
 namespace {
@@ -225,17 +249,25 @@ int check_workspace(void* ws, size_t bytes, const varlen_attn_layout& L) {
   return VARLEN_ATTN_OK;
 }
 
-int run_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const varlen_attn_tensor* k,
-            const varlen_attn_tensor* v, const varlen_attn_tensor* o,
-            const varlen_attn_tensor* lse, void* ws, size_t ws_bytes, int32_t* dev_status,
-            void* stream, unsigned stages) {
+// Host checks of a forward call's problem and tensors.
+int check_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+              const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+              const varlen_attn_tensor* o, const varlen_attn_tensor* lse) {
   int rc = check_problem(p);
   if (rc) return rc;
   if ((rc = check_tensor(q, p->h_q, p->head_dim, 2))) return rc;
   if ((rc = check_tensor(k, p->h_kv, p->head_dim, 2))) return rc;
   if ((rc = check_tensor(v, p->h_kv, p->head_dim, 2))) return rc;
   if ((rc = check_tensor(o, p->h_q, p->head_dim, 2))) return rc;
-  if ((rc = check_tensor(lse, p->h_q, 1, 4))) return rc;
+  return check_tensor(lse, p->h_q, 1, 4);
+}
+
+int run_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q, const varlen_attn_tensor* k,
+            const varlen_attn_tensor* v, const varlen_attn_tensor* o,
+            const varlen_attn_tensor* lse, void* ws, size_t ws_bytes, int32_t* dev_status,
+            void* stream, unsigned stages) {
+  int rc = check_fwd(p, q, k, v, o, lse);
+  if (rc) return rc;
   varlen_attn_layout L;
   if ((rc = fwd_layout(p, o, &L))) return rc;
   if (p->batch == 0) return VARLEN_ATTN_OK;
@@ -406,6 +438,27 @@ int varlen_attn_fwd(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                  STAGE_SETUP | STAGE_FWD);
 }
 
+int varlen_attn_fwd_noalloc(const varlen_attn_problem* p, const varlen_attn_tensor* q,
+                            const varlen_attn_tensor* k, const varlen_attn_tensor* v,
+                            const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
+                            int32_t* dev_status, void* stream) {
+  // Same checks and kernels as varlen_attn_fwd; the workspace is the static
+  // per-device array, so nothing is allocated.  The setup kernel zeroes the
+  // claim counters and rewrites every other region it reads, so the array's
+  // previous contents do not matter.
+  int rc = check_fwd(p, q, k, v, o, lse);
+  if (rc) return rc;
+  varlen_attn_layout L;
+  if ((rc = fwd_layout(p, o, &L))) return rc;
+  if (L.total_bytes > (int64_t)kNoAllocScratchBytes) return VARLEN_ATTN_ERR_SCRATCH;
+  if (p->batch == 0)
+    return run_fwd(p, q, k, v, o, lse, nullptr, 0, dev_status, stream, STAGE_SETUP | STAGE_FWD);
+  void* ws = noalloc_scratch();
+  if (!ws) return VARLEN_ATTN_ERR_HIP;
+  return run_fwd(p, q, k, v, o, lse, ws, kNoAllocScratchBytes, dev_status, stream,
+                 STAGE_SETUP | STAGE_FWD);
+}
+
 int varlen_attn_fwd_setup(const varlen_attn_problem* p, const varlen_attn_tensor* q,
                           const varlen_attn_tensor* k, const varlen_attn_tensor* v,
                           const varlen_attn_tensor* o, const varlen_attn_tensor* lse,
@@ -473,6 +526,9 @@ const char* varlen_attn_status_string(int code) {
     case VARLEN_ATTN_ERR_POLICY: return "default_policy must be 0, 1 or 2";
     case VARLEN_ATTN_ERR_WINDOW: return "window_size entries must be >= -1";
     case VARLEN_ATTN_ERR_DTYPE: return "dtype must be VARLEN_ATTN_BF16 or VARLEN_ATTN_F16";
+    case VARLEN_ATTN_ERR_SCRATCH:
+      return "the problem needs a larger forward workspace than the 4 MiB static scratch of "
+             "varlen_attn_fwd_noalloc (use varlen_attn_fwd with a workspace)";
     case VARLEN_ATTN_ERR_SCALE: return "scale must be finite";
     case VARLEN_ATTN_ERR_HIP: return "a HIP kernel launch failed";
     case VARLEN_ATTN_ERR_OFFSETS:
