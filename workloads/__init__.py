@@ -346,3 +346,34 @@ def random_window(rng: np.random.Generator, max_size: int) -> np.ndarray:
     w = rng.integers(0, max_size, size=(3, 2), endpoint=True)
     w[rng.integers(0, 3, size=(3, 2)) == 0] = -1
     return w.astype(np.int32)
+
+
+def aliased_batch(seed: int, *, docs: int = 3, max_doc: int = 300, chunks: int = 2,
+                  h_q: int = 4, h_kv: int = 2, dim: int = 64, shuffle: bool = True,
+                  with_grad: bool = True, dtype: str = "bf16", window=None) -> Batch:
+    """Context-parallel style batch: `docs` documents of random length, each
+    queried by `chunks` query segments that bind the document's key rows
+    (identical K/V/dK/dV offsets) with random per-segment q causal offsets;
+    the segments of all documents are shuffled, so aliasing segments need
+    not be adjacent.  Top-left causal with offsets; token-major LSE."""
+    rng = np.random.default_rng(seed)
+    dl = rng.integers(16, max_doc, size=docs, endpoint=True)
+    kv_start_doc = _with_gaps(dl, rng.integers(0, 8, size=docs, endpoint=True))
+    segs = []
+    for d in range(docs):
+        for _ in range(chunks):
+            lq = int(rng.integers(1, max(2, int(dl[d]) // chunks), endpoint=True))
+            off = int(rng.integers(-lq // 2, int(dl[d]) - lq + 1, endpoint=True))
+            segs.append((d, lq, off))
+    order = rng.permutation(len(segs)) if shuffle else np.arange(len(segs))
+    segs = [segs[i] for i in order]
+    lq = np.array([s[1] for s in segs], np.int64)
+    lk = np.array([int(dl[s[0]]) for s in segs], np.int64)
+    q_start = _with_gaps(lq, rng.integers(0, 4, size=len(segs), endpoint=True))
+    kv_start = np.array([int(kv_start_doc[s[0]]) for s in segs] + [int(kv_start_doc[-1])],
+                        np.int64)
+    qco = np.array([s[2] for s in segs], np.int32)
+    return build(f"aliased_{seed}", seed, h_q, h_kv, dim, lq, lk, q_start, kv_start,
+                 default_policy=CAUSAL_TOP_LEFT, q_causal_offset=qco, lse_kind="token",
+                 kv_rows=int(kv_start_doc[-1]), with_grad=with_grad, dtype=dtype,
+                 window=window)
