@@ -90,6 +90,13 @@ SETUP_CASES = [
     # more sequences (and kv groups) than the setup kernel ranks from LDS, and
     # tile lists longer than one block-scan chunk
     ("random_b1100", lambda: workloads.random_batch(300, batch=1100, max_len=12, max_gap=4)),
+    # batches that split the setup kernel's pairwise passes 8, 2 and 1 lanes
+    # per sequence (all ranked from LDS), and many aliased kv groups
+    ("random_b100", lambda: workloads.random_batch(302, batch=100, max_len=40, max_gap=4)),
+    ("random_b300", lambda: workloads.random_batch(303, batch=300, max_len=20, max_gap=4,
+                                                   q_causal_offset=True)),
+    ("random_b1000", lambda: workloads.random_batch(304, batch=1000, max_len=12, max_gap=3)),
+    ("aliased_b120", lambda: workloads.aliased_batch(305, docs=40, max_doc=60, chunks=3)),
     ("random_b2200", lambda: workloads.random_batch(301, batch=2200, max_len=6, max_gap=2,
                                                     cross=False)),
 ] + [(f"window{s}", (lambda s=s: workloads.random_batch(s, batch=9, max_len=600,
