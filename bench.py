@@ -184,6 +184,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-seconds", type=float, default=0.25,
+                    help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="packed_causal",
@@ -247,8 +249,17 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[-1].record()
 
-    for _ in range(args.warmup):
+    # Warm-up: the W steps asked for, and more until the GPU has run the step
+    # for args.warmup_seconds, so that the timed steps see the clocks and
+    # caches of a GPU under load (a few short steps do not get there: a
+    # 0.4 ms step measured 15 % slower after 3 warm-up steps than after 20).
+    warm = 0
+    t_warm = time.perf_counter()
+    while warm < args.warmup or time.perf_counter() - t_warm < args.warmup_seconds:
         step()
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     if int(dev.status.item()) != 0:
         print(f"device status {int(dev.status.item())}", file=sys.stderr)
@@ -304,6 +315,7 @@ def main(argv=None) -> int:
         })
     config["step_pct_peak"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
     config["wall_s_timed"] = round(t_wall, 3)
+    config["warmup_steps_run"] = warm
     line = {
         "metric": "varlen attention fwd/bwd TFLOP/s (causal-aware) and % of bf16 MFMA peak",
         "value": round(value, 2),
