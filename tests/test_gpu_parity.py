@@ -339,6 +339,32 @@ def test_many_queries_over_few_keys_gradients():
     check_backward(batch, dev, ref, rel=2.0 ** -8)
 
 
+@pytest.mark.timeout(600)
+def test_largest_legal_token_stride_fwd_bwd():
+    """Every 16-bit tensor with a token stride just below the largest the host
+    accepts (a 128-row tile's byte range under 2^31, about 8.45 M elements):
+    the kernels' 32-bit offsets inside a tile are then at their largest.  Key
+    lengths above 64 fill whole key and query tiles.  Forward and backward
+    against the oracle at the plain bars, pads untouched."""
+    h, d = 1, 128
+    n = ((1 << 30) - 128) // 127 // (h * d) - 1
+    st = (1 + n) * h * d
+    assert (127 * st + d) * 2 < 1 << 31 <= (127 * (st + h * d) + d) * 2
+    lq, lk = [36, 20], [70, 30]
+    start_q = np.concatenate([[0], np.cumsum(lq)])
+    start_k = np.concatenate([[0], np.cumsum(lk)])
+    gaps = {x: n for x in ("q", "k", "v", "o", "do", "dq", "dk", "dv")}
+    batch = workloads.build("largest_stride", 260, h, h, d, lq, lk, start_q, start_k,
+                            default_policy=2, lse_kind="head", token_gaps=gaps)
+    say(f"[largest stride] stride_t={st} elements, lq={lq} lk={lk}")
+    dev = _dev(batch)
+    dev.fwd()
+    dev.bwd()
+    torch.cuda.synchronize()
+    check_forward(batch, dev)
+    check_backward(batch, dev)
+
+
 def test_gqa_groups_of_four_fwd_bwd():
     batch = workloads.random_batch(300, batch=4, max_len=200, h_q=8, h_kv=2, dim=128)
     say(f"[gqa] lq={batch.lq.tolist()}")
